@@ -1,0 +1,327 @@
+"""Throughput of the Q4_K FFN hot path on one MI355X.
+
+Headline (``value``): effective weight-GB/s of the decode GEMV sweep, batch 1,
+Q4_K weights [n, k] with (n, k) in {(4096, 4096), (11008, 4096),
+(4096, 11008)}.  One step is one pass over the three GEMVs.  Weight bytes are
+the algorithmic 144 bytes per 256 weights.  Every step reads a different copy
+of each matrix (copies totalling >= 1 GiB per shape, four times the 256 MB
+Infinity Cache), inputs are resident in HBM before timing starts, and the K
+timed steps (and the W warmup steps) are each replayed from one HIP graph so
+that host launch overhead is not measured.
+
+Also reported (``secondary``): the 7B-style decode FFN at 1/4/8 tokens, the
+prefill FFN (Q8_1 + MMQ) at 512 and 2048 tokens in TOPS, the 64-expert top-8
+MoE decode FFN, and the roofline of the dominant kernel.  ``cpu_baseline``
+times the CPU oracle on a bounded sample of the headline workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5033.0        # dense int8 MFMA: 256 CU x 2.4 GHz x 8192 ops/clk
+ROTATE_BYTES = 1 << 30         # per rotated tensor set
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP events on torch's current stream (where the library launches)."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.torch.cuda.synchronize()
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.torch.cuda.synchronize()
+        self.ms = self.a.elapsed_time(self.b)
+
+
+def capture(fn, count):
+    """A HIP graph holding `count` calls fn(i)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn(0)                      # eager run before capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def rotated(tensor_np, total=ROTATE_BYTES, max_copies=None):
+    """Device copies of one byte array so that copies * size >= total."""
+    import torch
+    nbytes = tensor_np.nbytes
+    copies = max(2, -(-total // nbytes))
+    if max_copies:
+        copies = min(copies, max_copies)
+    base = torch.from_numpy(np.ascontiguousarray(tensor_np)).cuda()
+    stride = -(-nbytes // 256) * 256
+    buf = torch.empty(copies * stride, dtype=torch.uint8, device="cuda")
+    views = []
+    for c in range(copies):
+        v = buf[c * stride: c * stride + nbytes]
+        v.copy_(base)
+        views.append(v)
+    return views
+
+
+def timed_graph(fn, steps, warmup):
+    g_w = capture(fn, max(1, warmup)) if warmup > 0 else None
+    g_t = capture(fn, steps)
+    if g_w is not None:
+        g_w.replay()
+    with Timer() as t:
+        g_t.replay()
+    return t.ms
+
+
+# -- headline: GEMV sweep -----------------------------------------------------------
+
+def gemv_sweep(q4k, synth, steps, warmup):
+    import torch
+    shapes = []
+    for s, (n, k) in enumerate(synth.GEMV_SWEEP_SHAPES):
+        _, _, w, x = synth.gemv_sweep_case(s)
+        shapes.append(dict(n=n, k=k, w=rotated(w), x=torch.from_numpy(x).cuda(),
+                           y=torch.empty((1, n), dtype=torch.float32, device="cuda"),
+                           bytes=q4k.q4k_weight_bytes(n, k)))
+
+    def one_pass(i):
+        for sh in shapes:
+            ws = sh["w"][i % len(sh["w"])]
+            q4k.q4k_gemv(ws, sh["x"], sh["y"], 1, sh["n"], sh["k"])
+
+    ms = timed_graph(one_pass, steps, warmup)
+    total_bytes = steps * sum(sh["bytes"] for sh in shapes)
+    # per-shape average launch duration (graph of launches of one shape)
+    per_shape = []
+    for sh in shapes:
+        reps = len(sh["w"])
+
+        def one(i, sh=sh):
+            q4k.q4k_gemv(sh["w"][i % len(sh["w"])], sh["x"], sh["y"], 1, sh["n"], sh["k"])
+
+        g = capture(one, reps)
+        g.replay()
+        with Timer() as t:
+            g.replay()
+        us = t.ms * 1e3 / reps
+        per_shape.append(dict(n=sh["n"], k=sh["k"], bytes=sh["bytes"], us=us,
+                              gbs=sh["bytes"] / (us * 1e-6) / 1e9))
+    return ms, total_bytes, per_shape
+
+
+# -- secondary workloads -------------------------------------------------------------
+
+def decode_ffn(q4k, synth, reps=40):
+    import torch
+    hidden, inter = 4096, 11008
+    wg, wu, wd = synth.dense_ffn_weights(synth.DECODE_FFN_7B, hidden, inter)
+    per_ffn = 2 * q4k.q4k_weight_bytes(inter, hidden) + q4k.q4k_weight_bytes(hidden, inter)
+    cat = np.concatenate([wg, wu, wd])
+    copies = rotated(cat)
+    gb = q4k.q4k_weight_bytes(inter, hidden)
+    out = {}
+    for m in (1, 4, 8):
+        x = torch.from_numpy(synth.activations(synth.DECODE_FFN_7B, m, hidden, True, sub=m)).cuda()
+        y = torch.empty((m, hidden), dtype=torch.float32, device="cuda")
+        ws = torch.empty(q4k.ffn_swiglu_q4k_workspace_bytes(m, hidden, inter), dtype=torch.uint8,
+                         device="cuda")
+
+        def call(i):
+            c = copies[i % len(copies)]
+            q4k.ffn_swiglu_q4k(c[:gb], c[gb:2 * gb], c[2 * gb:], x, q4k.Q4K_F32, m, hidden, inter,
+                               y, ws)
+
+        ms = timed_graph(call, reps, 5)
+        us = ms * 1e3 / reps
+        out[f"m{m}"] = dict(us_per_ffn=round(us, 2), tokens_per_s=round(m / (us * 1e-6), 1),
+                            weight_gbs=round(per_ffn / (us * 1e-6) / 1e9, 1))
+    return out
+
+
+def prefill_ffn(q4k, synth, reps=4):
+    import torch
+    hidden, inter = 5120, 17408
+    wg, wu, wd = synth.dense_ffn_weights(synth.PREFILL_FFN, hidden, inter)
+    gb = q4k.q4k_weight_bytes(inter, hidden)
+    copies = rotated(np.concatenate([wg, wu, wd]), max_copies=7)
+    out = {}
+    for m in (512, 2048):
+        xb = synth.to_bf16_bits(synth.activations(synth.PREFILL_FFN, m, hidden, True, sub=m))
+        x = torch.from_numpy(xb.view(np.int16)).cuda()
+        y = torch.empty((m, hidden), dtype=torch.float32, device="cuda")
+        ws = torch.empty(q4k.ffn_swiglu_q4k_workspace_bytes(m, hidden, inter), dtype=torch.uint8,
+                         device="cuda")
+
+        def call(i):
+            c = copies[i % len(copies)]
+            q4k.ffn_swiglu_q4k(c[:gb], c[gb:2 * gb], c[2 * gb:], x, q4k.Q4K_BF16, m, hidden, inter,
+                               y, ws)
+
+        ms = timed_graph(call, reps, 1)
+        us = ms * 1e3 / reps
+        ops = 2.0 * m * (3 * hidden * inter)
+        out[f"m{m}"] = dict(us_per_ffn=round(us, 1), tops=round(ops / (us * 1e-6) / 1e12, 1),
+                            frac_int8_peak=round(ops / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4),
+                            tokens_per_s=round(m / (us * 1e-6), 1))
+    return out
+
+
+def moe_ffn(q4k, synth, reps=40):
+    import torch
+    n_exp, hidden, inter, m, k = 64, 2048, 768, 4, 8
+    bg, bu, bd = synth.moe_banks(synth.MOE_DECODE, n_exp, hidden, inter)
+    x = torch.from_numpy(synth.activations(synth.MOE_DECODE, m, hidden, False)).cuda()
+    ids_np, wts_np = synth.router(synth.MOE_DECODE, m, n_exp, k)
+    ids = torch.from_numpy(ids_np).cuda()
+    wts = torch.from_numpy(wts_np).cuda()
+    distinct = len(np.unique(ids_np))
+    per_expert = 3 * q4k.q4k_weight_bytes(inter, hidden)
+    bank = q4k.q4k_weight_bytes(inter, hidden) * n_exp
+    copies = rotated(np.concatenate([bg, bu, bd]))
+    y = torch.empty((m, hidden), dtype=torch.float32, device="cuda")
+    ws = torch.empty(q4k.ffn_swiglu_q4k_workspace_bytes(m, hidden, inter, k), dtype=torch.uint8,
+                     device="cuda")
+
+    def call(i):
+        c = copies[i % len(copies)]
+        q4k.ffn_swiglu_q4k(c[:bank], c[bank:2 * bank], c[2 * bank:], x, q4k.Q4K_F32, m, hidden,
+                           inter, y, ws, n_experts=n_exp, ids=ids, wts=wts, top_k=k)
+
+    ms = timed_graph(call, reps, 5)
+    us = ms * 1e3 / reps
+    return dict(distinct_experts=distinct, us_per_ffn=round(us, 2),
+                tokens_per_s=round(m / (us * 1e-6), 1),
+                weight_gbs=round(distinct * per_expert / (us * 1e-6) / 1e9, 1))
+
+
+# -- CPU oracle baseline ---------------------------------------------------------------
+
+def cpu_baseline(synth):
+    from oracle import q4k_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    cases = [synth.gemv_sweep_case(s) for s in range(3)]
+    total = 0
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        for n, k, w, x in cases:
+            orc.gemv(w, n, k, x)
+            total += orc.q4k_weight_bytes(n, k)
+        passes += 1
+        if time.perf_counter() - t0 > 10.0 or passes >= 5:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=round(total / dt / 1e9, 3), unit="GB/s", cores=cores, kind="oracle",
+                sample=f"{passes} pass(es) of the 3-shape batch-1 GEMV sweep through the f64 "
+                       f"numpy oracle (dequantise + matmul), {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--skip-secondary", action="store_true")
+    ap.add_argument("--skip-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gemm_block_q4_amd as q4k
+    from gemm_block_q4_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    q4k.load_library()
+    torch.cuda.set_device(0)
+
+    log("bench: GEMV sweep")
+    ms, total_bytes, per_shape = gemv_sweep(q4k, synth, args.steps, args.warmup)
+    value = total_bytes / (ms * 1e-3) / 1e9
+    log(f"bench: GEMV sweep {value:.1f} GB/s over {args.steps} steps ({ms:.3f} ms)")
+
+    sum_bytes = sum(p["bytes"] for p in per_shape)
+    sum_us = sum(p["us"] for p in per_shape)
+    achieved = sum_bytes / (sum_us * 1e-6) / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="gemv_kernel<1> (q4k_gemv, m=1)",
+                    per_shape=[dict(n=p["n"], k=p["k"], us=round(p["us"], 3), gbs=round(p["gbs"], 1))
+                               for p in per_shape])
+
+    secondary = {}
+    if not args.skip_secondary:
+        log("bench: decode FFN")
+        secondary["decode_ffn_4096_11008"] = decode_ffn(q4k, synth)
+        log("bench: prefill FFN")
+        secondary["prefill_ffn_5120_17408"] = prefill_ffn(q4k, synth)
+        log("bench: MoE")
+        secondary["moe_64x_top8_2048_768"] = moe_ffn(q4k, synth)
+
+    cpu = None
+    if not args.skip_cpu:
+        log("bench: CPU oracle baseline")
+        cpu = cpu_baseline(synth)
+
+    line = {
+        "metric": "Q4_K GEMV weight-GB/s (% HBM peak); MMQ prefill TOPS (% int8 MFMA peak)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMV sweep, batch 1, Q4_K [n,k] in "
+                               "{(4096,4096),(11008,4096),(4096,11008)}, x f32 N(0,1), seed 0",
+                   "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

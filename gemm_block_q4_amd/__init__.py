@@ -1,0 +1,25 @@
+"""MI355X (gfx950) Q4_K SwiGLU feed-forward library: Python binding.
+
+The compute lives in ``libq4k.so`` (hand-written HIP kernels behind the C ABI
+declared in ``include/q4k.h``).  This package only marshals torch tensors to
+device pointers and streams; it has no compute path of its own.  The shared
+library is loaded lazily on first use and a missing library raises an error.
+"""
+
+from ._binding import (  # noqa: F401
+    Q4K_BF16,
+    Q4K_F32,
+    Q4K_REGIME_AUTO,
+    Q4K_REGIME_DECODE,
+    Q4K_REGIME_PREFILL,
+    Q4KError,
+    ffn_swiglu_q4k,
+    ffn_swiglu_q4k_workspace_bytes,
+    library_path,
+    load_library,
+    q4k_gemv,
+    q4k_mmq,
+    q4k_test_mmq_partials,
+    q4k_weight_bytes,
+    q8_1_quantize,
+)

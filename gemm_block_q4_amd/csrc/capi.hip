@@ -1,0 +1,378 @@
+// C ABI of the Q4_K FFN library: argument validation, workspace layout and
+// dispatch.  Validation follows the pages' launchers: a null weight pointer is
+// rejected before any launch ("realizar -- q4k_gemv_cached_uses.rs",
+// q4k_gemv_indexed_async), k must be a multiple of 256 (q4k_gemv_cached), and
+// sizes are overflow-checked ("micro_moe.rs", elements / checked_mul).  No
+// HIP call happens before every argument check has passed.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/q4k.h"
+#include "q4k_device.hpp"
+#include "q4k_internal.hpp"
+
+using namespace q4k;
+
+namespace {
+
+constexpr size_t kAlign = 16;
+constexpr size_t kWsAlign = 256;
+constexpr int kMaxDevices = 64;
+// Decode path: the per-token sub-block sums and the per-row partials live in
+// LDS, which bounds the reduction length.
+constexpr int kDecodeMaxK = 32768;
+// Prefill path: 64 tokens per workgroup row of the grid (grid.y <= 65535).
+constexpr int kPrefillMaxM = 64 * 65535;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool mul_ok(size_t a, size_t b, size_t* out) {
+  if (a != 0 && b > SIZE_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// 0 unknown, 1 gfx950, 2 other; cached per device ordinal.
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return Q4K_ERR_DEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return Q4K_ERR_DEVICE;
+  int state = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return Q4K_ERR_DEVICE;
+    state = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(state, std::memory_order_relaxed);
+  }
+  return state == 1 ? Q4K_OK : Q4K_ERR_DEVICE;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH; }
+
+// Weight matrix [rows][cols] checks shared by every entry point.
+int check_matrix(int rows, int cols, size_t* bytes) {
+  if (rows < 1 || cols < Q4K_QK || cols % Q4K_QK != 0) return Q4K_ERR_SHAPE;
+  size_t blocks;
+  if (!mul_ok(static_cast<size_t>(rows), static_cast<size_t>(cols / Q4K_QK), &blocks)) return Q4K_ERR_OVERFLOW;
+  if (blocks > static_cast<size_t>(INT32_MAX)) return Q4K_ERR_OVERFLOW;  // 32-bit block indices
+  if (!mul_ok(blocks, Q4K_BLOCK_BYTES, bytes)) return Q4K_ERR_OVERFLOW;
+  return Q4K_OK;
+}
+
+int check_elems(int m, int k) {
+  size_t e;
+  if (!mul_ok(static_cast<size_t>(m), static_cast<size_t>(k), &e)) return Q4K_ERR_OVERFLOW;
+  if (e > static_cast<size_t>(INT32_MAX) * 4) return Q4K_ERR_OVERFLOW;  // grid of m*k/4 lanes fits
+  return Q4K_OK;
+}
+
+// Workspace layout of ffn_swiglu_q4k.
+struct FfnLayout {
+  size_t total = 0;
+  // decode dense
+  size_t h = 0;
+  // prefill
+  size_t qx = 0, dx = 0, qh = 0, dh = 0;
+  // MoE
+  size_t slot_expert = 0, slot_count = 0, slot_x = 0, slot_y = 0, y_pair = 0;
+  int slots = 0;
+};
+
+int resolve_regime(int regime, int m) {
+  if (regime == Q4K_REGIME_AUTO) return m <= Q4K_DECODE_MAX_TOKENS ? Q4K_REGIME_DECODE : Q4K_REGIME_PREFILL;
+  return regime;
+}
+
+bool ffn_layout(int m, int hidden, int inter, int top_k, int regime, FfnLayout* L) {
+  if (m < 1 || hidden < Q4K_QK || inter < Q4K_QK || hidden % Q4K_QK || inter % Q4K_QK) return false;
+  if (top_k < 0 || top_k > 64) return false;
+  regime = resolve_regime(regime, m);
+  if (regime != Q4K_REGIME_DECODE && regime != Q4K_REGIME_PREFILL) return false;
+  if (regime == Q4K_REGIME_DECODE && m > Q4K_DECODE_MAX_TOKENS) return false;
+  if (top_k > 0 && regime != Q4K_REGIME_DECODE) return false;
+  const size_t M = static_cast<size_t>(m), H = static_cast<size_t>(hidden), I = static_cast<size_t>(inter);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = round_up(off + bytes, kWsAlign);
+    return at;
+  };
+  if (top_k > 0) {
+    const size_t pairs = M * static_cast<size_t>(top_k);
+    L->slots = static_cast<int>(pairs);
+    L->slot_expert = take(pairs * 4);
+    L->slot_count = take(pairs * 4);
+    L->slot_x = take(pairs * kMaxTokens * 4);
+    L->slot_y = take(pairs * kMaxTokens * 4);
+    L->h = take(pairs * I * 4);
+    L->y_pair = take(pairs * H * 4);
+  } else if (regime == Q4K_REGIME_DECODE) {
+    L->h = take(M * I * 4);
+  } else {
+    if (M * H > (SIZE_MAX / 8) || M * I > (SIZE_MAX / 8)) return false;
+    L->qx = take(M * H);
+    L->dx = take(M * H / 32 * 4);
+    L->h = take(M * I * 4);
+    L->qh = take(M * I);
+    L->dh = take(M * I / 32 * 4);
+  }
+  L->total = off;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t q4k_weight_bytes(int rows, int cols) {
+  if (rows < 0 || cols < 0 || cols % Q4K_QK != 0) return 0;
+  size_t blocks, bytes;
+  if (!mul_ok(static_cast<size_t>(rows), static_cast<size_t>(cols / Q4K_QK), &blocks)) return 0;
+  if (!mul_ok(blocks, Q4K_BLOCK_BYTES, &bytes)) return 0;
+  return bytes;
+}
+
+const char* q4k_status_string(int status) {
+  switch (status) {
+    case Q4K_OK: return "ok";
+    case Q4K_ERR_NULL: return "a required pointer is NULL";
+    case Q4K_ERR_SHAPE: return "a size is out of range or not a required multiple";
+    case Q4K_ERR_ALIGN: return "a pointer is not aligned as required";
+    case Q4K_ERR_OVERFLOW: return "a derived size overflows";
+    case Q4K_ERR_WORKSPACE: return "workspace missing or too small";
+    case Q4K_ERR_LAUNCH: return "the HIP runtime reported a launch error";
+    case Q4K_ERR_DEVICE: return "the current device is not gfx950";
+    default: return "unknown status";
+  }
+}
+
+int q4k_gemv(const void* w, const float* x, float* y, int m, int n, int k, void* stream) {
+  if (!w || !x || !y) return Q4K_ERR_NULL;
+  if (m < 1 || m > Q4K_DECODE_MAX_TOKENS) return Q4K_ERR_SHAPE;
+  if (k > kDecodeMaxK) return Q4K_ERR_SHAPE;
+  size_t wbytes;
+  int st = check_matrix(n, k, &wbytes);
+  if (st) return st;
+  if ((st = check_elems(m, k)) || (st = check_elems(m, n))) return st;
+  if (!aligned(w, kAlign) || !aligned(x, kAlign) || !aligned(y, 4)) return Q4K_ERR_ALIGN;
+  if ((st = check_device())) return st;
+  GemvArgs a{};
+  a.w = static_cast<const uint8_t*>(w);
+  a.mat_bytes = wbytes;
+  a.x = x;
+  a.ldx = k;
+  a.y = y;
+  a.ldy = n;
+  a.n = n;
+  a.k = k;
+  a.m = m;
+  return launch_status(launch_gemv(a, static_cast<hipStream_t>(stream)));
+}
+
+int q8_1_quantize(const void* x, int x_dtype, int m, int k, int8_t* qs, uint32_t* ds,
+                  void* stream) {
+  if (!x || !qs || !ds) return Q4K_ERR_NULL;
+  if (x_dtype != Q4K_F32 && x_dtype != Q4K_BF16) return Q4K_ERR_SHAPE;
+  if (m < 1 || k < Q4K_Q8_1_BLOCK || k % Q4K_Q8_1_BLOCK != 0) return Q4K_ERR_SHAPE;
+  int st = check_elems(m, k);
+  if (st) return st;
+  if (!aligned(x, x_dtype == Q4K_F32 ? 16 : 8) || !aligned(qs, 4) || !aligned(ds, 4)) return Q4K_ERR_ALIGN;
+  if ((st = check_device())) return st;
+  return launch_status(launch_q8_1_quantize(x, x_dtype == Q4K_BF16, m, k, qs, ds,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+static int mmq_common(const void* w, const int8_t* qs, const uint32_t* ds, float* y,
+                      int32_t* partials, int m, int n, int k, void* stream) {
+  if (!w || !qs || (!partials && (!ds || !y))) return Q4K_ERR_NULL;
+  if (m < 1 || m > kPrefillMaxM) return Q4K_ERR_SHAPE;
+  size_t wbytes;
+  int st = check_matrix(n, k, &wbytes);
+  if (st) return st;
+  if ((st = check_elems(m, k)) || (st = check_elems(m, n))) return st;
+  if (partials) {
+    size_t e;
+    if (!mul_ok(static_cast<size_t>(m) * static_cast<size_t>(n), static_cast<size_t>(k / 32), &e)) return Q4K_ERR_OVERFLOW;
+  }
+  if (!aligned(w, kAlign) || !aligned(qs, kAlign) || (ds && !aligned(ds, 4)) ||
+      (y && !aligned(y, 4)) || (partials && !aligned(partials, 4)))
+    return Q4K_ERR_ALIGN;
+  if ((st = check_device())) return st;
+  MmqArgs a{};
+  a.w = static_cast<const uint8_t*>(w);
+  a.qs = qs;
+  a.ds = ds;
+  a.y = y;
+  a.partials = partials;
+  a.m = m;
+  a.n = n;
+  a.k = k;
+  return launch_status(launch_mmq(a, static_cast<hipStream_t>(stream)));
+}
+
+int q4k_mmq(const void* w, const int8_t* qs, const uint32_t* ds, float* y, int m, int n, int k,
+            void* stream) {
+  return mmq_common(w, qs, ds, y, nullptr, m, n, k, stream);
+}
+
+int q4k_test_mmq_partials(const void* w, const int8_t* qs, int m, int n, int k,
+                          int32_t* partials, void* stream) {
+  if (!partials) return Q4K_ERR_NULL;
+  return mmq_common(w, qs, nullptr, nullptr, partials, m, n, k, stream);
+}
+
+size_t ffn_swiglu_q4k_workspace_bytes(int m, int hidden, int inter, int top_k, int regime) {
+  FfnLayout L;
+  if (!ffn_layout(m, hidden, inter, top_k, regime, &L)) return 0;
+  return L.total;
+}
+
+int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int n_experts,
+                   const void* x, int x_dtype, int m, int hidden, int inter, const int32_t* ids,
+                   const float* wts, int top_k, int regime, float* y, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!w_gate || !w_up || !w_down || !x || !y) return Q4K_ERR_NULL;
+  if (x_dtype != Q4K_F32 && x_dtype != Q4K_BF16) return Q4K_ERR_SHAPE;
+  if (m < 1 || n_experts < 1) return Q4K_ERR_SHAPE;
+  const bool moe = ids != nullptr;
+  if (moe) {
+    if (!wts) return Q4K_ERR_NULL;
+    if (top_k < 1 || top_k > 64 || top_k > n_experts) return Q4K_ERR_SHAPE;
+  } else {
+    if (n_experts != 1 || (top_k != 0 && top_k != 1)) return Q4K_ERR_SHAPE;
+    top_k = 0;
+  }
+  if (regime < Q4K_REGIME_AUTO || regime > Q4K_REGIME_PREFILL) return Q4K_ERR_SHAPE;
+  const int reg = resolve_regime(regime, m);
+  if (reg == Q4K_REGIME_DECODE && m > Q4K_DECODE_MAX_TOKENS) return Q4K_ERR_SHAPE;
+  if (moe && reg != Q4K_REGIME_DECODE) return Q4K_ERR_SHAPE;
+  if (reg == Q4K_REGIME_DECODE && (hidden > kDecodeMaxK || inter > kDecodeMaxK)) return Q4K_ERR_SHAPE;
+  if (reg == Q4K_REGIME_PREFILL && m > kPrefillMaxM) return Q4K_ERR_SHAPE;
+  size_t gu_bytes, dn_bytes;
+  int st = check_matrix(inter, hidden, &gu_bytes);
+  if (st) return st;
+  if ((st = check_matrix(hidden, inter, &dn_bytes))) return st;
+  size_t bank;
+  if (!mul_ok(gu_bytes, static_cast<size_t>(n_experts), &bank) ||
+      !mul_ok(dn_bytes, static_cast<size_t>(n_experts), &bank))
+    return Q4K_ERR_OVERFLOW;
+  if ((st = check_elems(m, hidden)) || (st = check_elems(m, inter))) return st;
+  if (moe && ((st = check_elems(m * top_k, hidden)) || (st = check_elems(m * top_k, inter)))) return st;
+  FfnLayout L;
+  if (!ffn_layout(m, hidden, inter, top_k, reg, &L)) return Q4K_ERR_SHAPE;
+  if (!workspace || workspace_bytes < L.total) return Q4K_ERR_WORKSPACE;
+  if (!aligned(w_gate, kAlign) || !aligned(w_up, kAlign) || !aligned(w_down, kAlign) ||
+      !aligned(x, kAlign) || !aligned(y, 4) || !aligned(workspace, kAlign) ||
+      (ids && !aligned(ids, 4)) || (wts && !aligned(wts, 4)))
+    return Q4K_ERR_ALIGN;
+  if ((st = check_device())) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* h = reinterpret_cast<float*>(ws + L.h);
+
+  if (moe) {
+    SlotTable tab{reinterpret_cast<int32_t*>(ws + L.slot_expert), reinterpret_cast<int32_t*>(ws + L.slot_count),
+                  reinterpret_cast<int32_t*>(ws + L.slot_x), reinterpret_cast<int32_t*>(ws + L.slot_y)};
+    hipError_t e = launch_moe_route(ids, m, top_k, n_experts, tab, L.slots, s);
+    if (e != hipSuccess) return Q4K_ERR_LAUNCH;
+    const int cap = m < kMaxTokens ? m : kMaxTokens;
+    GemvArgs gu{};
+    gu.w = static_cast<const uint8_t*>(w_gate);
+    gu.w_up = static_cast<const uint8_t*>(w_up);
+    gu.mat_bytes = gu_bytes;
+    gu.x = x;
+    gu.x_bf16 = x_dtype == Q4K_BF16;
+    gu.ldx = hidden;
+    gu.y = h;
+    gu.ldy = inter;
+    gu.n = inter;
+    gu.k = hidden;
+    gu.m = cap;
+    gu.slot_expert = tab.expert;
+    gu.slot_count = tab.count;
+    gu.slot_x = tab.xrow;
+    gu.slot_y = tab.yrow;
+    gu.slots = L.slots;
+    if ((e = launch_gemv(gu, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
+    float* y_pair = reinterpret_cast<float*>(ws + L.y_pair);
+    GemvArgs dn = gu;
+    dn.w = static_cast<const uint8_t*>(w_down);
+    dn.w_up = nullptr;
+    dn.mat_bytes = dn_bytes;
+    dn.x = h;
+    dn.x_bf16 = 0;
+    dn.ldx = inter;
+    dn.y = y_pair;
+    dn.ldy = hidden;
+    dn.n = hidden;
+    dn.k = inter;
+    dn.slot_x = tab.yrow;  // the down pass reads the pair's own h row
+    if ((e = launch_gemv(dn, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
+    return launch_status(launch_moe_combine(y_pair, wts, ids, m, top_k, n_experts, hidden, y, s));
+  }
+
+  if (reg == Q4K_REGIME_DECODE) {
+    GemvArgs gu{};
+    gu.w = static_cast<const uint8_t*>(w_gate);
+    gu.w_up = static_cast<const uint8_t*>(w_up);
+    gu.mat_bytes = gu_bytes;
+    gu.x = x;
+    gu.x_bf16 = x_dtype == Q4K_BF16;
+    gu.ldx = hidden;
+    gu.y = h;
+    gu.ldy = inter;
+    gu.n = inter;
+    gu.k = hidden;
+    gu.m = m;
+    hipError_t e = launch_gemv(gu, s);
+    if (e != hipSuccess) return Q4K_ERR_LAUNCH;
+    GemvArgs dn{};
+    dn.w = static_cast<const uint8_t*>(w_down);
+    dn.mat_bytes = dn_bytes;
+    dn.x = h;
+    dn.ldx = inter;
+    dn.y = y;
+    dn.ldy = hidden;
+    dn.n = hidden;
+    dn.k = inter;
+    dn.m = m;
+    return launch_status(launch_gemv(dn, s));
+  }
+
+  // Prefill: x -> Q8_1 -> MMQ gate/up with silu*mul -> h -> Q8_1 -> MMQ down.
+  int8_t* qx = reinterpret_cast<int8_t*>(ws + L.qx);
+  uint32_t* dx = reinterpret_cast<uint32_t*>(ws + L.dx);
+  int8_t* qh = reinterpret_cast<int8_t*>(ws + L.qh);
+  uint32_t* dh = reinterpret_cast<uint32_t*>(ws + L.dh);
+  hipError_t e = launch_q8_1_quantize(x, x_dtype == Q4K_BF16, m, hidden, qx, dx, s);
+  if (e != hipSuccess) return Q4K_ERR_LAUNCH;
+  MmqArgs gu{};
+  gu.w = static_cast<const uint8_t*>(w_gate);
+  gu.w_up = static_cast<const uint8_t*>(w_up);
+  gu.qs = qx;
+  gu.ds = dx;
+  gu.y = h;
+  gu.m = m;
+  gu.n = inter;
+  gu.k = hidden;
+  if ((e = launch_mmq(gu, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
+  if ((e = launch_q8_1_quantize(h, 0, m, inter, qh, dh, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
+  MmqArgs dn{};
+  dn.w = static_cast<const uint8_t*>(w_down);
+  dn.qs = qh;
+  dn.ds = dh;
+  dn.y = y;
+  dn.m = m;
+  dn.n = hidden;
+  dn.k = inter;
+  return launch_status(launch_mmq(dn, s));
+}
+
+}  // extern "C"

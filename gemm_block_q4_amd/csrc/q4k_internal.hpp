@@ -1,0 +1,65 @@
+// Host-side launchers shared between the C ABI layer and the kernel files.
+// All launchers assume validated arguments and return the HIP error of the
+// launch (hipSuccess when nothing went wrong).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q4k {
+
+// Routing table of the MoE decode path (device memory, written by the route
+// kernel).  Slot i holds up to kMaxTokens (pair) entries of one expert.
+struct SlotTable {
+  int32_t* expert;  // [slots]  expert id, -1 = unused slot
+  int32_t* count;   // [slots]  entries in the slot
+  int32_t* xrow;    // [slots][8] input row of each entry
+  int32_t* yrow;    // [slots][8] output row of each entry
+};
+
+// GEMV over one or many (expert, token set) slots.
+struct GemvArgs {
+  const uint8_t* w;      // weight bank (expert 0 at offset 0)
+  const uint8_t* w_up;   // up bank for the fused gate/up pass, else nullptr
+  size_t mat_bytes;      // bytes per expert matrix
+  const void* x;         // activations, row stride ldx elements
+  int x_bf16;            // 1: x holds bf16 values, 0: f32
+  int ldx;
+  float* y;              // output, row stride ldy
+  int ldy;
+  int n;                 // output rows per matrix
+  int k;                 // input columns (multiple of 256)
+  int m;                 // dense mode: tokens (rows of x / y)
+  const int32_t* slot_expert;  // nullptr: dense mode (single slot, expert 0)
+  const int32_t* slot_count;
+  const int32_t* slot_x;
+  const int32_t* slot_y;
+  int slots;
+};
+
+hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
+
+hipError_t launch_q8_1_quantize(const void* x, int x_bf16, int m, int k, int8_t* qs,
+                                uint32_t* ds, hipStream_t stream);
+
+struct MmqArgs {
+  const uint8_t* w;      // gate (or single) weights [n][k/256]
+  const uint8_t* w_up;   // up weights for the fused SwiGLU pass, else nullptr
+  const int8_t* qs;      // Q8_1 quants [m][k]
+  const uint32_t* ds;    // Q8_1 scale/sum words [m][k/32]
+  float* y;              // [m][n] f32 (h = silu(g) * u when w_up is set)
+  int32_t* partials;     // test hook: [m][n][k/32] int32 instead of y
+  int m, n, k;
+};
+
+hipError_t launch_mmq(const MmqArgs& a, hipStream_t stream);
+
+hipError_t launch_moe_route(const int32_t* ids, int m, int top_k, int n_experts,
+                            const SlotTable& t, int slots, hipStream_t stream);
+
+hipError_t launch_moe_combine(const float* y_pair, const float* wts, const int32_t* ids,
+                              int m, int top_k, int n_experts, int hidden, float* y,
+                              hipStream_t stream);
+
+}  // namespace q4k

@@ -1,0 +1,170 @@
+/*
+ * q4k.h -- C ABI of the MI355X (gfx950) Q4_K SwiGLU feed-forward library.
+ *
+ * The library computes the feed-forward block y = down(silu(gate(x)) * up(x))
+ * with weights stored as GGML-style block_q4_K, in two regimes: a
+ * dequant-fused GEMV for a few tokens (decode) and a Q8_1-activation x Q4_K
+ * integer GEMM (MMQ) for many tokens (prefill).  Sources, by page title:
+ *   - "realizar 0.8.5 -- src/cuda/executor/layers/ffn.rs": fused_ffn_swiglu_gpu
+ *     (the FFN), fused_ffn_swiglu_gpu_true_dp4a (Q8_1 activations, per-block
+ *     scale + 32 int8, scales applied after the integer dot).
+ *   - "realizar 0.8.5 -- src/cuda/executor/q4k_gemv_cached_uses.rs":
+ *     q4k_gemv_cached / _async (Q4_K GEMV, f32 x of length k, f32 y of length
+ *     n, k divisible by 256) and q4k_gemv_indexed_async (a null weight pointer
+ *     is rejected before any launch).
+ *   - "spark_model/layers/ops/q4k_mmq.rs": QK_K = 256, Q4K_BLOCK_BYTES = 144,
+ *     q4k_weight_bytes, quantize_act_q8_1, q4k_mmq_gemm (C = A_q8 x W_q4k^T),
+ *     and the prefill pipeline in the file header.
+ *   - "libmir-cuda 0.1.0 -- .../nvfp4/selected/micro_moe.rs":
+ *     DirectNvFp4MoeBf16::execute (top-k MoE: selected expert ids and a
+ *     routing weight per selection) and validate / elements (bank shapes,
+ *     overflow-checked sizes).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers must point to device memory of the
+ *     current HIP device; the caller owns every buffer and keeps it alive until
+ *     the stream has run the call.  The library allocates nothing and keeps no
+ *     state between calls.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call is
+ *     asynchronous on it; nothing synchronises inside the library.
+ *   - Arguments are validated on the host before any launch; on error nothing
+ *     is launched and a q4k_status code is returned.  Q4K_ERR_LAUNCH reports
+ *     a failure returned by the HIP runtime after a launch.
+ *   - Weight matrices, activations, quantised activations and the workspace
+ *     must be 16-byte aligned (a 144-byte block is nine 16-byte words, so all
+ *     blocks stay aligned).  Routing ids and weights need 4-byte alignment.
+ *   - Calls are reentrant: no global state is written.
+ *
+ * block_q4_K (GGML layout): bytes 0-1 fp16 d, 2-3 fp16 dmin, 4-15 twelve
+ * bytes of packed 6-bit (scale, min) pairs for eight 32-weight sub-blocks,
+ * 16-143 the 256 4-bit quants (weight 64g+l is the low nibble of byte 32g+l,
+ * weight 64g+32+l its high nibble).  Weight value: d*sc_j*q - dmin*m_j.
+ * A Q4_K matrix [rows][cols] stores row r's blocks at
+ * r*(cols/256) ... r*(cols/256) + cols/256 - 1 (row-major).
+ *
+ * Q8_1 (planar layout of this library): qs int8 [m][k] row-major and ds
+ * uint32 [m][k/32], where bits 0-15 hold the binary16 scale d and bits 16-31
+ * hold the block sum S = sum of the 32 quants as int16 (two's complement).
+ */
+#ifndef Q4K_H
+#define Q4K_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weights per super-block and bytes per block_q4_K ("q4k_mmq.rs", QK_K and
+   Q4K_BLOCK_BYTES). */
+#define Q4K_QK 256
+#define Q4K_BLOCK_BYTES 144
+/* Values per Q8_1 activation block ("ffn.rs", DP4A FFN doc). */
+#define Q4K_Q8_1_BLOCK 32
+/* Most tokens the decode regime (dequant-fused GEMV) takes per call. */
+#define Q4K_DECODE_MAX_TOKENS 8
+
+typedef enum {
+  Q4K_OK = 0,
+  Q4K_ERR_NULL = 1,      /* a required pointer is NULL */
+  Q4K_ERR_SHAPE = 2,     /* a size is out of range or not a required multiple */
+  Q4K_ERR_ALIGN = 3,     /* a pointer is not aligned as required */
+  Q4K_ERR_OVERFLOW = 4,  /* a derived size overflows */
+  Q4K_ERR_WORKSPACE = 5, /* workspace NULL or smaller than required */
+  Q4K_ERR_LAUNCH = 6,    /* the HIP runtime reported an error for a launch */
+  Q4K_ERR_DEVICE = 7     /* the current device is not gfx950 */
+} q4k_status;
+
+typedef enum { Q4K_F32 = 0, Q4K_BF16 = 1 } q4k_dtype;
+
+typedef enum {
+  Q4K_REGIME_AUTO = 0,    /* decode when m <= Q4K_DECODE_MAX_TOKENS, else prefill */
+  Q4K_REGIME_DECODE = 1,  /* f32 activations, dequant-fused GEMV */
+  Q4K_REGIME_PREFILL = 2  /* Q8_1 activations, integer MMQ */
+} q4k_regime;
+
+/* Host.  Bytes of a Q4_K matrix [rows][cols]: rows * (cols/256) * 144
+   ("q4k_mmq.rs", q4k_weight_bytes).  Returns 0 when rows < 0, cols < 0,
+   cols % 256 != 0 or the size overflows. */
+size_t q4k_weight_bytes(int rows, int cols);
+
+/* Host.  Static description of a status code (never NULL). */
+const char* q4k_status_string(int status);
+
+/* Decode GEMV ("q4k_gemv_cached_uses.rs", q4k_gemv_cached_async):
+     y[t][j] = sum_i dequant(w)[j][i] * x[t][i]   for t < m, j < n.
+   w: device, block_q4_K [n][k/256]; x: device f32 [m][k] row-major;
+   y: device f32 [m][n] row-major, overwritten.  1 <= m <= 8, n >= 1,
+   256 <= k <= 32768, k % 256 == 0.  Accumulation is f32 (the f32 activations are
+   split exactly enough that max |err| / (||w_j|| ||x_t||) stays near 2^-22).
+   Errors: Q4K_ERR_NULL, Q4K_ERR_SHAPE, Q4K_ERR_ALIGN, Q4K_ERR_OVERFLOW,
+   Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */
+int q4k_gemv(const void* w, const float* x, float* y, int m, int n, int k, void* stream);
+
+/* Q8_1 activation quantisation ("q4k_mmq.rs", quantize_act_q8_1; "ffn.rs",
+   q8_quantize_async): for each row t and 32-value block b of x,
+     amax = max |x|, d = amax / 127 (binary32), q = rint(x / d) (binary32
+     division, half to even), ds = binary16(d) | (sum q) << 16;
+   an all-zero block stores q = 0 and ds = 0.  Bit-exact by construction.
+   x: device [m][k] of x_dtype (Q4K_F32 or Q4K_BF16, bf16 widened exactly);
+   qs: device int8 [m][k]; ds: device uint32 [m][k/32].  m >= 1, k >= 32,
+   k % 32 == 0.  Inputs must be finite (non-finite input gives undefined
+   codes but never faults). */
+int q8_1_quantize(const void* x, int x_dtype, int m, int k, int8_t* qs, uint32_t* ds,
+                  void* stream);
+
+/* Prefill integer GEMM ("q4k_mmq.rs", q4k_mmq_gemm: C[m,n] = A_q8[m,k] x
+   W_q4k[n,k]^T; "ffn.rs", DP4A FFN doc: integer dot, then scales):
+     P[t][j][b] = sum_{i<32} q_w[j][32b+i] * q_a[t][32b+i]      (int32, exact)
+     y[t][j] = sum_b (d*sc)[j][b] * d_a[t][b] * P - (dmin*m)[j][b] * d_a[t][b] * S[t][b]
+   w: device block_q4_K [n][k/256]; qs/ds: device Q8_1 of the activations
+   [m][k] (as written by q8_1_quantize); y: device f32 [m][n], overwritten.
+   1 <= m <= 64 * 65535, n >= 1, k >= 256, k % 256 == 0.  Integer products are exact
+   (int8 MFMA); scales are applied in f32. */
+int q4k_mmq(const void* w, const int8_t* qs, const uint32_t* ds, float* y, int m, int n,
+            int k, void* stream);
+
+/* Test hook on the same device code as q4k_mmq: writes the integer partials
+   partials[t][j][b] = P[t][j][b] (int32 [m][n][k/32], device) instead of y.
+   Same shape rules as q4k_mmq; meant for small shapes. */
+int q4k_test_mmq_partials(const void* w, const int8_t* qs, int m, int n, int k,
+                          int32_t* partials, void* stream);
+
+/* Host.  Workspace bytes ffn_swiglu_q4k needs for these sizes and regime
+   (Q4K_REGIME_AUTO resolves by m as the call does); top_k = 0 for a dense
+   FFN.  Returns 0 for invalid sizes. */
+size_t ffn_swiglu_q4k_workspace_bytes(int m, int hidden, int inter, int top_k, int regime);
+
+/* SwiGLU feed-forward block ("ffn.rs", fused_ffn_swiglu_gpu and
+   fused_ffn_swiglu_gpu_true_dp4a; "q4k_mmq.rs" prefill pipeline;
+   "micro_moe.rs" for the MoE form):
+     dense (ids == NULL, n_experts == 1):
+       y[t] = W_down . (silu(W_gate . x[t]) * (W_up . x[t]))
+     MoE (ids != NULL):
+       y[t] = sum_{s < top_k} wts[t][s] * FFN_{ids[t][s]}(x[t])   (slot order)
+   w_gate, w_up: device banks of n_experts block_q4_K matrices [inter][hidden];
+   w_down: device bank of n_experts matrices [hidden][inter]; expert e's matrix
+   starts at e * q4k_weight_bytes(rows, cols) in its bank ("micro_moe.rs",
+   validate: gate and up equal, down transposed).
+   x: device [m][hidden] of x_dtype; y: device f32 [m][hidden], overwritten.
+   ids: device int32 [m][top_k]; wts: device f32 [m][top_k].  An id outside
+   [0, n_experts) contributes nothing (device data is not read back).
+   Regime: decode = f32 activations through the dequant-fused GEMV (gate and
+   up in one pass with silu*mul fused); prefill = x -> Q8_1 -> MMQ gate/up
+   with fused silu*mul -> h -> Q8_1 -> MMQ down.  MoE needs the decode regime
+   (m <= 8).  hidden, inter: multiples of 256 (at most 32768 in the decode
+   regime).
+   workspace: device, at least ffn_swiglu_q4k_workspace_bytes(...) bytes.
+   Errors: Q4K_ERR_NULL, Q4K_ERR_SHAPE, Q4K_ERR_ALIGN, Q4K_ERR_OVERFLOW,
+   Q4K_ERR_WORKSPACE, Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */
+int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int n_experts,
+                   const void* x, int x_dtype, int m, int hidden, int inter,
+                   const int32_t* ids, const float* wts, int top_k, int regime, float* y,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4K_H */

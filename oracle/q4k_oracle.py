@@ -257,9 +257,11 @@ def mmq_partials_token(w: np.ndarray, rows: int, cols: int, qs_t: np.ndarray,
     """
     if fields is None:
         fields = block_fields(w, rows, cols)
-    q = fields[4].reshape(rows, cols).astype(np.int64)
-    prod = q * np.asarray(qs_t, dtype=np.int64)[None, :]
-    return prod.reshape(rows, cols // SUB_BLOCK, SUB_BLOCK).sum(axis=-1)
+    # |q_w * q_a| <= 15 * 127 fits int16 and a 32-term sum fits int32, so the
+    # narrow integer types below are exact
+    q = fields[4].reshape(rows, cols).astype(np.int16)
+    prod = q * np.asarray(qs_t, dtype=np.int16)[None, :]
+    return prod.reshape(rows, cols // SUB_BLOCK, SUB_BLOCK).sum(axis=-1, dtype=np.int64)
 
 
 def mmq_partials(w: np.ndarray, rows: int, cols: int, qs: np.ndarray) -> np.ndarray:

@@ -1,0 +1,112 @@
+"""The C ABI library loads, exports every symbol its header declares, and
+rejects bad arguments on the host before any HIP call (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gemm_block_q4_amd import _binding as B
+from oracle import q4k_oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4k.h")
+
+# Fake, aligned, never dereferenced device addresses: every call below fails
+# validation before the library touches the HIP runtime.
+P = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", text)) - {"if", "sizeof"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.library_path()):
+        pytest.fail("libq4k.so is not built (run __graft_entry__.build())")
+    return B.load_library()
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert {"q4k_gemv", "q8_1_quantize", "q4k_mmq", "ffn_swiglu_q4k", "q4k_weight_bytes",
+            "q4k_status_string", "ffn_swiglu_q4k_workspace_bytes",
+            "q4k_test_mmq_partials"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_weight_bytes_matches_oracle(lib):
+    for rows, cols in ((768, 256), (4096, 11008), (17408, 5120), (2048, 768)):
+        assert lib.q4k_weight_bytes(rows, cols) == orc.q4k_weight_bytes(rows, cols)
+    assert lib.q4k_weight_bytes(4, 300) == 0
+    assert lib.q4k_weight_bytes(-1, 256) == 0
+
+
+def test_status_strings(lib):
+    for s in range(0, 8):
+        assert lib.q4k_status_string(s)
+    assert lib.q4k_status_string(99) == b"unknown status"
+
+
+def test_gemv_validation(lib):
+    assert lib.q4k_gemv(None, P, P, 1, 16, 256, None) == 1
+    assert lib.q4k_gemv(P, P, P, 0, 16, 256, None) == 2
+    assert lib.q4k_gemv(P, P, P, 9, 16, 256, None) == 2
+    assert lib.q4k_gemv(P, P, P, 1, 16, 300, None) == 2      # k not a multiple of 256
+    assert lib.q4k_gemv(P, P, P, 1, 0, 256, None) == 2
+    assert lib.q4k_gemv(P + 4, P, P, 1, 16, 256, None) == 3  # misaligned weights
+    assert lib.q4k_gemv(P, P, P, 1, 1 << 30, 32768, None) == 4    # block count overflows
+    assert lib.q4k_gemv(P, P, P, 1, 16, 32768 + 256, None) == 2   # k above the decode limit
+
+
+def test_q8_1_validation(lib):
+    assert lib.q8_1_quantize(None, 0, 1, 32, P, P, None) == 1
+    assert lib.q8_1_quantize(P, 2, 1, 32, P, P, None) == 2
+    assert lib.q8_1_quantize(P, 0, 1, 48, P, P, None) == 2
+    assert lib.q8_1_quantize(P + 4, 0, 1, 32, P, P, None) == 3
+
+
+def test_mmq_validation(lib):
+    assert lib.q4k_mmq(P, None, P, P, 1, 1, 256, None) == 1
+    assert lib.q4k_mmq(P, P, P, P, 1, 1, 512 + 32, None) == 2
+    assert lib.q4k_mmq(P, P + 1, P, P, 1, 1, 256, None) == 3
+    assert lib.q4k_test_mmq_partials(P, P, 1, 1, 256, None, None) == 1
+
+
+def test_ffn_validation(lib):
+    f = lib.ffn_swiglu_q4k
+    ws = lib.ffn_swiglu_q4k_workspace_bytes(1, 256, 768, 0, 0)
+    assert ws > 0
+    # null weights
+    assert f(None, P, P, 1, P, 0, 1, 256, 768, None, None, 0, 0, P, P, ws, None) == 1
+    # hidden not a multiple of 256
+    assert f(P, P, P, 1, P, 0, 1, 300, 768, None, None, 0, 0, P, P, ws, None) == 2
+    # dense call with several experts
+    assert f(P, P, P, 2, P, 0, 1, 256, 768, None, None, 0, 0, P, P, ws, None) == 2
+    # MoE without routing weights
+    assert f(P, P, P, 4, P, 0, 1, 256, 768, P, None, 2, 0, P, P, ws, None) == 1
+    # MoE top_k larger than the expert count
+    assert f(P, P, P, 4, P, 0, 1, 256, 768, P, P, 5, 0, P, P, ws, None) == 2
+    # MoE forced into the prefill regime
+    assert f(P, P, P, 4, P, 0, 1, 256, 768, P, P, 2, 2, P, P, ws, None) == 2
+    # decode regime forced with too many tokens
+    assert f(P, P, P, 1, P, 0, 9, 256, 768, None, None, 0, 1, P, P, ws, None) == 2
+    # workspace too small / missing
+    assert f(P, P, P, 1, P, 0, 1, 256, 768, None, None, 0, 0, P, P, ws - 1, None) == 5
+    assert f(P, P, P, 1, P, 0, 1, 256, 768, None, None, 0, 0, P, None, ws, None) == 5
+
+
+def test_workspace_sizes(lib):
+    w = lib.ffn_swiglu_q4k_workspace_bytes
+    assert w(1, 4096, 11008, 0, 0) >= 11008 * 4
+    assert w(8, 4096, 11008, 0, 0) >= 8 * 11008 * 4
+    pre = w(512, 5120, 17408, 0, 0)
+    assert pre >= 512 * (5120 + 5120 // 32 * 4 + 17408 * 4 + 17408 + 17408 // 32 * 4)
+    assert w(4, 2048, 768, 8, 0) >= 32 * (768 + 2048) * 4
+    assert w(0, 256, 256, 0, 0) == 0
+    assert w(9, 256, 256, 0, 1) == 0      # decode regime caps m at 8
+    assert w(4, 256, 256, 2, 2) == 0      # MoE is decode-only

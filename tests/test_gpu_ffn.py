@@ -1,0 +1,119 @@
+"""End-to-end SwiGLU FFN on the GPU: relative L2 <= 2e-3 against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import gemm_block_q4_amd as q4kmod
+from gemm_block_q4_amd import synth
+from oracle import q4k_oracle as orc
+from gpu_helpers import dev, empty, host, say, workspace
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def ffn_gpu(q4k, wg, wu, wd, x, hidden, inter, regime=0, bf16=False):
+    m = x.shape[0]
+    y = empty((m, hidden), torch.float32)
+    ws = workspace(q4k, m, hidden, inter, 0, regime)
+    xin = dev(synth.to_bf16_bits(x).view(np.int16)) if bf16 else dev(x)
+    q4k.ffn_swiglu_q4k(dev(wg), dev(wu), dev(wd), xin, q4k.Q4K_BF16 if bf16 else q4k.Q4K_F32,
+                       m, hidden, inter, y, ws, regime=regime)
+    return host(y)
+
+
+def test_tiny_ffn(lib):
+    say("ffn tiny 256/768 m=1")
+    wg, wu, wd = synth.dense_ffn_weights(synth.TINY_FFN, 256, 768)
+    x = synth.activations(synth.TINY_FFN, 1, 256, outliers=False)
+    y = ffn_gpu(lib, wg, wu, wd, x, 256, 768)
+    assert orc.relative_l2(y, orc.ffn_decode(wg, wu, wd, 256, 768, x)) <= TOL
+
+
+@pytest.fixture(scope="module")
+def decode7b():
+    return synth.dense_ffn_weights(synth.DECODE_FFN_7B, 4096, 11008)
+
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_decode_ffn_7b(lib, decode7b, m):
+    say(f"ffn decode 4096/11008 m={m}")
+    wg, wu, wd = decode7b
+    x = synth.activations(synth.DECODE_FFN_7B, m, 4096, outliers=True, sub=m)
+    y = ffn_gpu(lib, wg, wu, wd, x, 4096, 11008)
+    ref = orc.ffn_decode(wg, wu, wd, 4096, 11008, x)
+    assert orc.relative_l2(y, ref) <= TOL
+
+
+@pytest.mark.parametrize("m,regime", [(9, 0), (65, 0), (130, 0), (3, 2), (1, 2)])
+def test_prefill_ffn_small(lib, m, regime):
+    say(f"ffn prefill 512/768 m={m} regime={regime}")
+    hidden, inter = 512, 768
+    wg, wu, wd = synth.dense_ffn_weights(90, hidden, inter)
+    x = synth.activations(90, m, hidden, outliers=True, sub=m)
+    y = ffn_gpu(lib, wg, wu, wd, x, hidden, inter, regime=regime, bf16=True)
+    xb = synth.bf16_bits_to_f32(synth.to_bf16_bits(x))
+    ref = orc.ffn_prefill(wg, wu, wd, hidden, inter, xb)
+    assert orc.relative_l2(y, ref) <= TOL
+
+
+def test_decode_regime_forced_m8_matches(lib):
+    say("ffn decode regime forced, m=8, 512/768")
+    hidden, inter = 512, 768
+    wg, wu, wd = synth.dense_ffn_weights(91, hidden, inter)
+    x = synth.activations(91, 8, hidden, outliers=True)
+    y = ffn_gpu(lib, wg, wu, wd, x, hidden, inter, regime=1)
+    assert orc.relative_l2(y, orc.ffn_decode(wg, wu, wd, hidden, inter, x)) <= TOL
+
+
+@pytest.fixture(scope="module")
+def prefill_weights():
+    return synth.dense_ffn_weights(synth.PREFILL_FFN, 5120, 17408)
+
+
+@pytest.mark.parametrize("m,tokens", [(512, [0, 255, 511]), (2048, [1, 1024, 2047])])
+def test_prefill_ffn_full_size(lib, prefill_weights, m, tokens):
+    say(f"ffn prefill 5120/17408 m={m} (sampled tokens {tokens})")
+    wg, wu, wd = prefill_weights
+    x = synth.activations(synth.PREFILL_FFN, m, 5120, outliers=True, sub=m)
+    y = ffn_gpu(lib, wg, wu, wd, x, 5120, 17408, bf16=True)
+    xb = synth.bf16_bits_to_f32(synth.to_bf16_bits(x))
+    ref = orc.ffn_prefill(wg, wu, wd, 5120, 17408, xb, tokens=tokens)
+    assert orc.relative_l2(y[tokens], ref) <= TOL
+    assert np.all(np.isfinite(y))
+
+
+def moe_gpu(q4k, banks, x, ids, wts, n_exp, hidden, inter):
+    m, top_k = ids.shape
+    y = empty((m, hidden), torch.float32)
+    ws = workspace(q4k, m, hidden, inter, top_k, 0)
+    bg, bu, bd = banks
+    q4k.ffn_swiglu_q4k(dev(bg), dev(bu), dev(bd), dev(x), q4k.Q4K_F32, m, hidden, inter, y, ws,
+                       n_experts=n_exp, ids=dev(ids), wts=dev(wts), top_k=top_k)
+    return host(y)
+
+
+def test_moe_decode_config(lib):
+    say("moe 64 experts top-8, 4 tokens, 2048/768")
+    n_exp, hidden, inter, m, k = 64, 2048, 768, 4, 8
+    banks = synth.moe_banks(synth.MOE_DECODE, n_exp, hidden, inter)
+    x = synth.activations(synth.MOE_DECODE, m, hidden, outliers=False)
+    ids, wts = synth.router(synth.MOE_DECODE, m, n_exp, k)
+    y = moe_gpu(lib, banks, x, ids, wts, n_exp, hidden, inter)
+    ref = orc.moe_decode(*banks, n_exp, hidden, inter, x, ids, wts)
+    assert orc.relative_l2(y, ref) <= TOL
+
+
+def test_moe_duplicates_and_out_of_range_ids(lib):
+    say("moe duplicate and out-of-range ids")
+    n_exp, hidden, inter, m, k = 5, 256, 512, 3, 4
+    banks = synth.moe_banks(92, n_exp, hidden, inter)
+    x = synth.activations(92, m, hidden, outliers=True)
+    ids = np.array([[1, 1, 4, 9], [0, 2, -1, 2], [3, 3, 3, 3]], dtype=np.int32)
+    wts = np.array([[0.5, 0.25, 0.125, 2.0], [1.0, 0.5, 3.0, -1.0], [0.1, 0.2, 0.3, 0.4]],
+                   dtype=np.float32)
+    y = moe_gpu(lib, banks, x, ids, wts, n_exp, hidden, inter)
+    valid = (ids >= 0) & (ids < n_exp)
+    ref = orc.moe_decode(*banks, n_exp, hidden, inter, x, np.where(valid, ids, 0),
+                         np.where(valid, wts, 0).astype(np.float32))
+    assert orc.relative_l2(y, ref) <= TOL

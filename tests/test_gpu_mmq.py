@@ -1,0 +1,83 @@
+"""Prefill MMQ on the GPU: bit-exact integer partials, normwise parity 1e-5."""
+import numpy as np
+import pytest
+import torch
+
+from gemm_block_q4_amd import synth
+from oracle import q4k_oracle as orc
+from gpu_helpers import dev, empty, host, say
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+def quantised(m, k, seed, bf16=False):
+    x = synth.activations(80 + seed, m, k, outliers=True)
+    if bf16:
+        x = synth.bf16_bits_to_f32(synth.to_bf16_bits(x))
+    return orc.q8_1_quantize(x)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 256), (3, 5, 512), (65, 70, 256), (129, 64, 768)])
+def test_partials_bit_exact(lib, m, n, k):
+    say(f"mmq partials m={m} n={n} k={k}")
+    w = synth.random_q4k(synth.rng(81, 1, m + n), n, k)
+    qs, _, _ = quantised(m, k, m)
+    p = empty((m, n, k // 32), torch.int32)
+    lib.q4k_test_mmq_partials(dev(w), dev(qs), m, n, k, p)
+    assert np.array_equal(host(p).astype(np.int64), orc.mmq_partials(w, n, k, qs))
+
+
+def mmq_gpu(q4k, w, qs, d16, s, n, k):
+    m = qs.shape[0]
+    y = empty((m, n), torch.float32)
+    ds = orc.pack_ds(d16, s).view(np.int32)
+    q4k.q4k_mmq(dev(w), dev(qs), dev(ds), y, m, n, k)
+    return host(y)
+
+
+def test_integer_special_case_bit_exact(lib):
+    # d = 1, sc = 1, dmin = 0 weights and d16 = 1 activations: y is the
+    # integer product of the quants, exact in f32 (|y| < 2^24)
+    say("mmq integer special case")
+    n, k, m = 70, 768, 67
+    rng = np.random.default_rng(82)
+    blocks = np.zeros((n * k // 256, 144), dtype=np.uint8)
+    blocks[:, 0:2] = np.array([0x3C00], dtype=np.uint16).view(np.uint8)
+    blocks[:, 4:16] = orc.pack_scale_min(np.ones((1, 8), int), rng.integers(0, 64, (1, 8)))
+    blocks[:, 16:] = rng.integers(0, 256, (n * k // 256, 128), dtype=np.uint8)
+    w = blocks.reshape(-1)
+    qa = rng.integers(-127, 128, (m, k)).astype(np.int8)
+    d16 = np.ones((m, k // 32), dtype=np.float16)
+    ssum = qa.reshape(m, k // 32, 32).astype(np.int64).sum(-1).astype(np.int16)
+    y = mmq_gpu(lib, w, qa, d16, ssum, n, k)
+    qw = orc.unpack_quants(blocks[:, 16:]).reshape(n, k).astype(np.int64)
+    assert np.array_equal(y.astype(np.float64), (qa.astype(np.int64) @ qw.T).astype(np.float64))
+
+
+def check(q4k, w, qs, d16, s, n, k, tokens=None):
+    y = mmq_gpu(q4k, w, qs, d16, s, n, k)
+    tokens = list(range(qs.shape[0])) if tokens is None else tokens
+    ref = orc.mmq(w, n, k, qs, d16, s, tokens=tokens)
+    xn = np.linalg.norm(orc.q8_1_dequantize(qs[tokens], d16[tokens]), axis=1)
+    err = orc.normalized_max_error(y[tokens], ref, orc.row_norms(w, n, k), xn)
+    assert err <= TOL, err
+    return y
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 3, 256), (64, 64, 512), (130, 200, 1024), (7, 129, 2048)])
+def test_mmq_small(lib, m, n, k):
+    say(f"mmq m={m} n={n} k={k}")
+    w = synth.random_q4k(synth.rng(83, 1, m * 3 + n), n, k)
+    qs, d16, s = quantised(m, k, n)
+    check(lib, w, qs, d16, s, n, k)
+
+
+def test_mmq_prefill_gate_full_size(lib):
+    n, k, m = 17408, 5120, 512
+    say(f"mmq full size m={m} n={n} k={k} (sampled tokens)")
+    w = synth.random_q4k(synth.rng(84, 1), n, k)
+    qs, d16, s = quantised(m, k, 7, bf16=True)
+    y1 = check(lib, w, qs, d16, s, n, k, tokens=[0, 63, 64, 300, 511])
+    y2 = mmq_gpu(lib, w, qs, d16, s, n, k)
+    assert np.array_equal(y1, y2)
