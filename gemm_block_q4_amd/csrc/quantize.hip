@@ -5,7 +5,8 @@
 // values; quantised once and shared by gate and up).  Per 32-value block:
 // amax = max |x|, d = amax / 127 in binary32, q = rint(x / d) (binary32
 // division, round half to even), stored d as binary16 (nearest even) and the
-// exact integer block sum S.  The kernel is memory-bound: one lane owns four
+// exact integer block sum S (a scale that would overflow binary16 saturates
+// at 65504 and quantises the block).  The kernel is memory-bound: one lane owns four
 // consecutive values, eight lanes (an aligned DPP row quarter) own a block and
 // combine their max and sum with three xor shuffles.
 #include "q4k_device.hpp"
@@ -39,7 +40,10 @@ __global__ __launch_bounds__(256) void q8_1_quantize_kernel(const void* __restri
   amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
   amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
   amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
-  const float d = amax / 127.0f;  // correctly rounded binary32 division
+  float d = amax / 127.0f;  // correctly rounded binary32 division
+  // A scale whose binary16 rounding would overflow saturates at the largest
+  // finite binary16 value, and the block is quantised with that stored scale.
+  if (d >= 65520.0f) d = 65504.0f;
   int q[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {

@@ -106,7 +106,9 @@ int q4k_gemv(const void* w, const float* x, float* y, int m, int n, int k, void*
    q8_quantize_async): for each row t and 32-value block b of x,
      amax = max |x|, d = amax / 127 (binary32), q = rint(x / d) (binary32
      division, half to even), ds = binary16(d) | (sum q) << 16;
-   an all-zero block stores q = 0 and ds = 0.  Bit-exact by construction.
+   an all-zero block stores q = 0 and ds = 0; a block with d >= 65520 (whose
+   binary16 rounding would overflow) stores d = 65504 and is quantised with
+   it, so values beyond 127 * 65504 clamp to +-127.  Bit-exact by construction.
    x: device [m][k] of x_dtype (Q4K_F32 or Q4K_BF16, bf16 widened exactly);
    qs: device int8 [m][k]; ds: device uint32 [m][k/32].  m >= 1, k >= 32,
    k % 32 == 0.  Inputs must be finite (non-finite input gives undefined

@@ -39,8 +39,10 @@ design notes of the repository):
   at 4-15, 128 bytes of 4-bit quants at 16-143.  A weight is
   ``d*sc_j*q - dmin*m_j`` for its 32-weight sub-block j.
 * Q8_1: per 32 values, ``d = amax/127`` in binary32, ``q = round-half-even(x/d)``
-  in binary32, the scale stored as binary16 (round to nearest even) and the
-  block sum stored as the exact integer ``S = sum(q)`` (int16).  A binary16
+  in binary32, the scale stored as binary16 (round to nearest even,
+  saturating at 65504 when the rounding would overflow, in which case the
+  block is quantised with 65504) and the block sum stored as the exact
+  integer ``S = sum(q)`` (int16).  A binary16
   block sum ``fp16(d*S)`` overflows for the prefill intermediate activations
   of the synthetic workload, so the integer is kept instead.
 * The MMQ result is the reference dot
@@ -67,6 +69,10 @@ SUB_BLOCK = 32
 #: Values per Q8_1 activation block ("ffn.rs", doc of the DP4A FFN: a
 #: per-block scale and 32 int8 values).
 Q8_1_BLOCK = 32
+#: Largest finite binary16 value and the smallest binary32 value that rounds
+#: (to nearest even) past it to infinity.
+F16_MAX = 65504.0
+F16_OVERFLOW = 65520.0
 
 
 def q4k_weight_bytes(rows: int, cols: int) -> int:
@@ -201,7 +207,10 @@ def q8_1_quantize(x: np.ndarray):
       division in binary32 and rounding half to even (clamped to +-127, a
       guard that never fires);
     * stored: ``d16 = binary16(d)`` (round to nearest even, subnormals kept)
-      and the exact block sum ``S = sum q_i``.
+      and the exact block sum ``S = sum q_i``;
+    * if ``binary16(d)`` would overflow (``d >= 65520``), the scale saturates:
+      ``d = 65504`` is stored and used as the divisor, so values beyond
+      127 * 65504 clamp to +-127 (the pages leave scale overflow open).
 
     Returns ``qs`` int8 [m, k], ``d16`` float16 [m, k/32], ``S`` int16
     [m, k/32].  Input must be finite.
@@ -215,6 +224,10 @@ def q8_1_quantize(x: np.ndarray):
     xb = x.reshape(m, k // Q8_1_BLOCK, Q8_1_BLOCK)
     amax = np.max(np.abs(xb), axis=-1)                       # float32, exact
     d = amax / np.float32(127.0)                             # binary32 RNE
+    # a scale whose binary16 rounding would overflow saturates at 65504 and
+    # the block is quantised with that stored scale instead
+    sat = d >= F16_OVERFLOW
+    d = np.where(sat, np.float32(F16_MAX), d).astype(np.float32)
     safe = np.where(amax > 0, d, np.float32(1.0)).astype(np.float32)
     ratio = (xb / safe[..., None]).astype(np.float32)        # binary32 RNE
     q = np.clip(np.rint(ratio), -127, 127)                   # half to even

@@ -107,5 +107,7 @@ def q8_1_block(xs: list[float]) -> tuple[list[int], float, int]:
     if amax == 0:
         return [0] * len(xs), 0.0, 0
     d = f32(amax / 127.0)
+    if d >= 65520.0:          # binary16 would overflow: saturate the scale
+        d = 65504.0
     q = [max(-127, min(127, rint_even(f32(v / d)))) for v in xs]
     return q, f16(d), sum(q)

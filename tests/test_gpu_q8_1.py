@@ -17,6 +17,7 @@ def mixed(m, k, seed):
         x[2, 32:64] = np.float32(1e-30)
         x[3, 64:96] = np.linspace(-3e4, 3e4, 32, dtype=np.float32)
         x[0, 96:128] = np.float32(-2.0 ** -100)
+        x[2, 128:160] = np.linspace(-2e7, 9e6, 32, dtype=np.float32)   # saturated scale
     return x
 
 

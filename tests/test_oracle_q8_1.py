@@ -28,6 +28,7 @@ def _mixed_inputs():
     x[4, 96:128] = np.float32(1e-30)                    # tiny values
     x[5, 128:160] = np.linspace(-3e4, 3e4, 32, dtype=np.float32)
     x[6, :32] = np.float32(2.0 ** -140)                 # subnormal binary32 inputs
+    x[7, 160:192] = np.linspace(-2e7, 9e6, 32, dtype=np.float32)   # saturated scale
     return x
 
 
@@ -62,11 +63,15 @@ def test_invariants():
     # scale is a normal binary32 number; a subnormal scale loses precision and
     # the clamp to 127 can then fire)
     d32 = (amax.astype(np.float32) / np.float32(127.0)).astype(np.float64)
-    normal = d32 >= 2.0 ** -126
+    normal = (d32 >= 2.0 ** -126) & (d32 < 65520.0)
     err = np.abs(xb - d32[..., None] * qb)
     assert np.all((err <= 0.5 * d32[..., None] * (1 + 2.0 ** -20))[normal])
     # stored sum is the exact integer sum
     assert np.array_equal(s.astype(np.int64), qb.sum(-1))
+    # saturated blocks store the largest finite binary16 scale
+    sat = d32 >= 65520.0
+    assert sat.any() and np.all(d16[sat] == np.float16(65504.0))
+    assert np.all(np.isfinite(d16.astype(np.float64)))
 
 
 def test_exact_ties_round_to_even():
