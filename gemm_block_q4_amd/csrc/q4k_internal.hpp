@@ -38,7 +38,10 @@ struct GemvArgs {
   int slots;
 };
 
+// Dispatches to the VALU kernel (few tokens) or the matrix-core kernel.
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
+hipError_t launch_gemv_valu(const GemvArgs& a, hipStream_t stream);
+hipError_t launch_gemv_mfma(const GemvArgs& a, hipStream_t stream);
 
 hipError_t launch_q8_1_quantize(const void* x, int x_bf16, int m, int k, int8_t* qs,
                                 uint32_t* ds, hipStream_t stream);
