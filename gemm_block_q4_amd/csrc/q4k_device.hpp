@@ -62,6 +62,32 @@ __device__ __forceinline__ void scale_min_rt(const uint4& h, int s, uint32_t& sc
   mn = upper ? mn_hi : mn_lo;
 }
 
+// Raw buffer loads.  A lane whose byte offset (plus the instruction's
+// constant offset) is at or past the resource's size reads zeros and sends no
+// memory request, so a load is predicated without a branch.  (A branch around
+// a load makes the compiler copy the result at the join, which waits for the
+// load right after issuing it and serialises every prefetch.)
+typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr uint32_t kOob = 0x80000000u;  // above every resource size used here
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // 32-bit data format, raw (stride 0) access
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), static_cast<int>(kRsrcWord3));
+}
+
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+  const v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint2 buf_load8(rsrc_t r, uint32_t off) {
+  const v2u32 v = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, 0);
+  return make_uint2(v.x, v.y);
+}
+
 // Sum over the 64 lanes of a wavefront (every lane gets the total).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

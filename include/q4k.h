@@ -96,8 +96,12 @@ const char* q4k_status_string(int status);
      y[t][j] = sum_i dequant(w)[j][i] * x[t][i]   for t < m, j < n.
    w: device, block_q4_K [n][k/256]; x: device f32 [m][k] row-major;
    y: device f32 [m][n] row-major, overwritten.  1 <= m <= 8, n >= 1,
-   256 <= k <= 32768, k % 256 == 0.  Accumulation is f32 (the f32 activations are
-   split exactly enough that max |err| / (||w_j|| ||x_t||) stays near 2^-22).
+   256 <= k <= 32768, k % 256 == 0.  Weights are never rounded.  For one token
+   each 64-value slice of x is held as an integer with 21 significant bits
+   relative to the slice maximum (exact integer dot products, f32 scaling and
+   accumulation); for 2..8 tokens x is split into two binary16 parts for the
+   matrix cores.  Either way max |err| / (||w_j|| ||x_t||) stays far below
+   1e-5.  A non-finite x gives non-finite outputs.
    Errors: Q4K_ERR_NULL, Q4K_ERR_SHAPE, Q4K_ERR_ALIGN, Q4K_ERR_OVERFLOW,
    Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */
 int q4k_gemv(const void* w, const float* x, float* y, int m, int n, int k, void* stream);
