@@ -1,4 +1,4 @@
-// Dequant-fused Q4_K GEMV on the matrix cores (3..8 tokens), gfx950.
+// Dequant-fused Q4_K GEMV on the matrix cores (2..8 tokens), gfx950.
 //
 // "realizar -- q4k_gemv_cached_uses.rs", q4k_gemv_cached_async: y = W x with
 // W in block_q4_K [n][k/256] and f32 x of length k; "realizar -- ffn.rs",
@@ -16,8 +16,11 @@
 //    multiplied by dmin;
 //  * activations: per token and 256-block, x is scaled by 2^sh (sh chosen so
 //    the block maximum lands in [2^14, 2^15)) and split into two binary16
-//    halves hi + lo that carry 22 significant bits; both halves go through
-//    the same weight operand, and the block result is scaled back by 2^-sh.
+//    halves hi + lo that carry 22 significant bits.  The 16 rows of the
+//    activation operand hold the hi halves of tokens 0..7 (rows 0..7) and the
+//    lo halves (rows 8..15), so one MFMA per step multiplies both halves of
+//    every token by the same weight operand; the two result rows of a token
+//    are added at the end.
 // The relative error of a row result is thus a few 2^-22 of ||w|| ||x||.
 //
 // Work decomposition: a workgroup (4 wavefronts) owns 16 output rows; the
@@ -25,10 +28,11 @@
 // Lane l holds weight row n0 + l%16 and the 64 weights 64*(l/16) .. +63 of
 // each block (32 contiguous quant bytes, two 16-byte loads), i.e. the K
 // index 8*(l/16)+i of step s is weight 64*(l/16) + 8*s + i; the activation
-// operand uses the same K mapping with the token in place of the row.  Each
-// wavefront converts its own activation range, four blocks at a time, into
-// LDS in operand layout (all 64 lanes convert, then lanes read their
-// operands), so no cross-wavefront synchronisation is needed until the four
+// operand uses the same K mapping.  Each wavefront converts its own
+// activation range a chunk of blocks at a time into LDS in operand layout.
+// Every global load is a raw buffer load (out-of-range lanes read zero), all
+// loads of a chunk are issued before any of them is used, and reductions
+// across lanes use DPP, so a chunk costs one memory latency.  The four
 // partial tiles are added in a fixed order at the end (deterministic).
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
@@ -43,21 +47,26 @@ typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kRows = 16;     // output rows per workgroup (MFMA N)
-constexpr int kChunk = 4;     // blocks converted per LDS round
+constexpr int kRows = 16;  // output rows per workgroup (MFMA N)
 
-// LDS of one wavefront's activation operands for a chunk, MT tokens:
-//   hi / lo: [kChunk][8 steps][4 lane groups][MT] x 8 halves (16 B per entry)
-//   xs_hi / xs_lo: [kChunk][4 lane groups][MT] two halves (X_{2g}, X_{2g+1})
-//   shift: [kChunk][16] exponent sh per token (entries >= MT unused)
+// Tokens per half of the activation operand (4 or 8), and blocks converted
+// per LDS round (the chunk's activation loads, MT * CH float4 per lane, stay
+// within 64 registers).
+template <int MT> constexpr int half_rows() { return MT <= 4 ? 4 : 8; }
+template <int MT> constexpr int chunk_blocks() { return MT <= 4 ? 4 : 2; }
+
+// LDS of one wavefront's activation operands for a chunk, R2 = 2 * half_rows:
+//   op: [CH][8 steps][4 lane groups][R2 rows] x 8 halves (16 B per entry);
+//       rows 0..HR-1 hold the hi halves of the tokens, rows HR..R2-1 the lo
+//   xs: [CH][4 lane groups][R2 rows] two halves (X_{2g}, X_{2g+1}) * 2^-6
+//   shift: [CH][8] exponent sh per token
 template <int MT>
 struct WaveLds {
-  static constexpr int kOp = kChunk * 8 * 4 * MT;
-  uint4 hi[kOp];
-  uint4 lo[kOp];
-  uint32_t xs_hi[kChunk * 4 * MT];
-  uint32_t xs_lo[kChunk * 4 * MT];
-  int shift[kChunk * 16];
+  static constexpr int kCH = chunk_blocks<MT>();
+  static constexpr int kR2 = 2 * half_rows<MT>();
+  uint4 op[kCH * 8 * 4 * kR2];
+  uint32_t xs[kCH * 4 * kR2];
+  int shift[kCH * 8];
 };
 
 template <int MT, bool GU>
@@ -68,14 +77,18 @@ struct Lds {
   };
 };
 
+// Four activations at element offset `off` of the activation buffer (kOob:
+// zeros).
 template <bool BF16>
-__device__ __forceinline__ float4 load_x4(const void* x, size_t idx) {
+__device__ __forceinline__ float4 load_x4(rsrc_t r, uint32_t off) {
   if constexpr (BF16) {
-    const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + idx);
+    const uint2 raw = buf_load8(r, off == kOob ? kOob : 2u * off);
     return make_float4(bf16_bits_to_float(raw.x & 0xFFFFu), bf16_bits_to_float(raw.x >> 16),
                        bf16_bits_to_float(raw.y & 0xFFFFu), bf16_bits_to_float(raw.y >> 16));
   } else {
-    return *reinterpret_cast<const float4*>(static_cast<const float*>(x) + idx);
+    const uint4 raw = buf_load16(r, off == kOob ? kOob : 4u * off);
+    return make_float4(__uint_as_float(raw.x), __uint_as_float(raw.y), __uint_as_float(raw.z),
+                       __uint_as_float(raw.w));
   }
 }
 
@@ -84,10 +97,22 @@ __device__ __forceinline__ uint32_t pack_half2(_Float16 a, _Float16 b) {
          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xF, true));
+}
+
+// Maximum of non-negative values over the wavefront, in every lane (lanes
+// outside a DPP row read 0, the identity here).
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));        // quad_perm(1,0,3,2)
+  v = fmaxf(v, dpp<0x4E>(v));        // quad_perm(2,3,0,1)
+  v = fmaxf(v, dpp<0x114>(v));       // row_shr:4
+  v = fmaxf(v, dpp<0x118>(v));       // row_shr:8
+  v = fmaxf(v, dpp<0x142, 0xA>(v));  // row_bcast:15
+  v = fmaxf(v, dpp<0x143, 0xC>(v));  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // Exponent that maps a block maximum into [2^14, 2^15) (0 for an all-zero
@@ -103,24 +128,30 @@ __device__ __forceinline__ void split_half(float v, _Float16& hi, _Float16& lo) 
   lo = static_cast<_Float16>(v - static_cast<float>(hi));
 }
 
-// Converts this wavefront's activations of blocks [b0, b0 + nb) into operand
-// layout.  Lane l owns values 4l .. 4l+3 of each 256-block: operand step
-// s = (l % 16) / 2, lane group g = l / 16, halves 4*(l%2) .. +3, sub-block
-// j = l / 8.
-template <int MT, bool BF16>
-__device__ __forceinline__ void convert_chunk(WaveLds<MT>& L, const void* __restrict__ x,
-                                              const int* xrow, int ldx, int mt, int b0, int nb,
-                                              int lane) {
+// Converts loaded activations of one chunk into operand layout.  Lane l owns
+// values 4l .. 4l+3 of each 256-block: operand step s = (l % 16) / 2, lane
+// group g = l / 16, halves 4*(l%2) .. +3, sub-block j = l / 8.  Tokens at or
+// past the live count `mt` and blocks past `nb` are skipped (uniform branches):
+// their operand rows hold stale values, which only reach result rows that are
+// never read.
+template <int MT>
+__device__ __forceinline__ void convert_chunk(WaveLds<MT>& L, const float4 (&xv)[MT][WaveLds<MT>::kCH],
+                                              int mt, int nb, int lane) {
+  constexpr int CH = WaveLds<MT>::kCH;
+  constexpr int R2 = WaveLds<MT>::kR2;
+  constexpr int HR = R2 / 2;
   const int s = (lane & 15) >> 1;
   const int g = lane >> 4;
   const int half = lane & 1;
-  for (int t = 0; t < MT; ++t) {
-    if (t >= mt) break;
-    for (int bi = 0; bi < nb; ++bi) {
-      const float4 v = load_x4<BF16>(x, static_cast<size_t>(xrow[t]) * ldx +
-                                            static_cast<size_t>(b0 + bi) * kQK + 4 * lane);
+#pragma unroll
+  for (int bi = 0; bi < CH; ++bi) {
+    if (bi >= nb) break;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      if (t >= mt) break;
+      const float4 v = xv[t][bi];
       float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-      amax = wave_max(amax);
+      amax = wave_max_nonneg(amax);
       const int sh = block_shift(amax);
       const float v0 = ldexpf(v.x, sh), v1 = ldexpf(v.y, sh);
       const float v2 = ldexpf(v.z, sh), v3 = ldexpf(v.w, sh);
@@ -129,25 +160,26 @@ __device__ __forceinline__ void convert_chunk(WaveLds<MT>& L, const void* __rest
       split_half(v1, h1, l1);
       split_half(v2, h2, l2);
       split_half(v3, h3, l3);
-      const int e = ((bi * 8 + s) * 4 + g) * MT + t;
-      reinterpret_cast<uint2*>(&L.hi[e])[half] = make_uint2(pack_half2(h0, h1), pack_half2(h2, h3));
-      reinterpret_cast<uint2*>(&L.lo[e])[half] = make_uint2(pack_half2(l0, l1), pack_half2(l2, l3));
-      // sum of the scaled values of sub-block j = lane / 8 (eight lanes)
+      const int e = ((bi * 8 + s) * 4 + g) * R2 + t;
+      reinterpret_cast<uint2*>(&L.op[e])[half] = make_uint2(pack_half2(h0, h1), pack_half2(h2, h3));
+      reinterpret_cast<uint2*>(&L.op[e + HR])[half] = make_uint2(pack_half2(l0, l1), pack_half2(l2, l3));
+      // sum of the scaled values of sub-block j = lane / 8 (an aligned octet
+      // of one DPP row): lanes 8j+4 .. 8j+7 end with the octet's sum
       float xs = (v0 + v1) + (v2 + v3);
-      xs += __shfl_xor(xs, 1, 64);
-      xs += __shfl_xor(xs, 2, 64);
-      xs += __shfl_xor(xs, 4, 64);
-      if ((lane & 7) == 0) {
+      xs += dpp<0xB1>(xs);
+      xs += dpp<0x4E>(xs);
+      xs += dpp<0x114>(xs);
+      if ((lane & 7) == 7) {
         const int j = lane >> 3;  // sub-block: lane group j/2, K slot j%2
         // |xs| < 32 * 2^15; the sum is stored as xs * 2^-6 (the mins are
         // used as m * 2^6 <= 4032, still exact) to stay inside binary16
         _Float16 xh, xl;
         split_half(xs * 0.015625f, xh, xl);
-        const int ei = (bi * 4 + (j >> 1)) * MT + t;
-        reinterpret_cast<uint16_t*>(&L.xs_hi[ei])[j & 1] = __builtin_bit_cast(uint16_t, xh);
-        reinterpret_cast<uint16_t*>(&L.xs_lo[ei])[j & 1] = __builtin_bit_cast(uint16_t, xl);
+        const int ei = (bi * 4 + (j >> 1)) * R2 + t;
+        reinterpret_cast<uint16_t*>(&L.xs[ei])[j & 1] = __builtin_bit_cast(uint16_t, xh);
+        reinterpret_cast<uint16_t*>(&L.xs[ei + HR])[j & 1] = __builtin_bit_cast(uint16_t, xl);
       }
-      if (lane == 0) L.shift[bi * 16 + t] = sh;
+      if (lane == 0) L.shift[bi * 8 + t] = sh;
     }
   }
 }
@@ -175,17 +207,19 @@ struct BlockRegs {
   uint4 q1;  // quant bytes 32g+16 .. 32g+31
 };
 
-__device__ __forceinline__ void load_block(const uint8_t* __restrict__ blk, int g, BlockRegs& r) {
-  r.h = *reinterpret_cast<const uint4*>(blk);
-  r.q0 = *reinterpret_cast<const uint4*>(blk + 16 + 32 * g);
-  r.q1 = *reinterpret_cast<const uint4*>(blk + 32 + 32 * g);
+// The block at byte offset `off` of the resource, lane group g (kOob: zeros).
+__device__ __forceinline__ void load_block(rsrc_t r, uint32_t off, int g, BlockRegs& b) {
+  b.h = buf_load16(r, off);
+  const uint32_t q = off + 32u * static_cast<uint32_t>(g);
+  b.q0 = buf_load16(r, q + 16u);
+  b.q1 = buf_load16(r, q + 32u);
 }
 
 // One block of one matrix: the main chain (cm) and the min term (cn).
 template <int MT>
 __device__ __forceinline__ void block_mfma(const BlockRegs& r, int g, const WaveLds<MT>& L, int bi,
-                                           int tok, bool active, float& d, float& dmin,
-                                           v4f& cm, v4f& cn) {
+                                           int arow, float& d, float& dmin, v4f& cm, v4f& cn) {
+  constexpr int R2 = WaveLds<MT>::kR2;
   d = half_bits_to_float(r.h.x & 0xFFFFu);
   dmin = half_bits_to_float(r.h.x >> 16);
   uint32_t sc0, mn0, sc1, mn1;
@@ -203,29 +237,17 @@ __device__ __forceinline__ void block_mfma(const BlockRegs& r, int g, const Wave
   for (int s = 0; s < 8; ++s) {
     const v8h b = s < 4 ? weights8(w[2 * s], w[2 * s + 1], s0, o0)
                         : weights8(w[2 * (s - 4)] >> 4, w[2 * (s - 4) + 1] >> 4, s1, o1);
-    v8h ah = v8h{0, 0, 0, 0, 0, 0, 0, 0}, al = ah;
-    if (active) {
-      const int e = ((bi * 8 + s) * 4 + g) * MT + tok;
-      ah = __builtin_bit_cast(v8h, L.hi[e]);
-      al = __builtin_bit_cast(v8h, L.lo[e]);
-    }
-    cm = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, b, cm, 0, 0, 0);
-    cm = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, b, cm, 0, 0, 0);
+    const v8h av = __builtin_bit_cast(v8h, L.op[((bi * 8 + s) * 4 + g) * R2 + arow]);
+    cm = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b, cm, 0, 0, 0);
   }
   // min term: K slots 0 and 1 of lane group g hold (m_{2g}, m_{2g+1}) and the
   // activation sums (X_{2g}, X_{2g+1}); the other slots are zero
   const v8h bm = v8h{static_cast<_Float16>(64.0f * static_cast<float>(mn0)),
                      static_cast<_Float16>(64.0f * static_cast<float>(mn1)), 0, 0, 0, 0, 0, 0};
-  v8h xh = v8h{0, 0, 0, 0, 0, 0, 0, 0}, xl = xh;
-  if (active) {
-    const v2h ph = __builtin_bit_cast(v2h, L.xs_hi[(bi * 4 + g) * MT + tok]);
-    const v2h pl = __builtin_bit_cast(v2h, L.xs_lo[(bi * 4 + g) * MT + tok]);
-    xh[0] = ph[0]; xh[1] = ph[1];
-    xl[0] = pl[0]; xl[1] = pl[1];
-  }
+  const v2h px = __builtin_bit_cast(v2h, L.xs[(bi * 4 + g) * R2 + arow]);
+  const v8h xm = v8h{px[0], px[1], 0, 0, 0, 0, 0, 0};
   cn = v4f{0.f, 0.f, 0.f, 0.f};
-  cn = __builtin_amdgcn_mfma_f32_16x16x32_f16(xh, bm, cn, 0, 0, 0);
-  cn = __builtin_amdgcn_mfma_f32_16x16x32_f16(xl, bm, cn, 0, 0, 0);
+  cn = __builtin_amdgcn_mfma_f32_16x16x32_f16(xm, bm, cn, 0, 0, 0);
 }
 
 __device__ __forceinline__ void lds_fence() {
@@ -237,6 +259,9 @@ __device__ __forceinline__ void lds_fence() {
 
 template <int MT, bool GU, bool BF16>
 __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(GemvArgs a) {
+  constexpr int CH = WaveLds<MT>::kCH;
+  constexpr int R2 = WaveLds<MT>::kR2;
+  constexpr int HR = R2 / 2;
   __shared__ Lds<MT, GU> lds;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -265,46 +290,68 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(GemvArgs a) {
   }
 
   const int n0 = blockIdx.x * kRows;
-  const int nl = lane & 15;   // B operand weight row / A operand token / C row-slot
+  const int rows = min(kRows, a.n - n0);
+  const int nl = lane & 15;   // B operand weight row / A operand row / C column
   const int g = lane >> 4;    // lane group: K slots 8g .. 8g+7
-  const int row = min(n0 + nl, a.n - 1);
-  const size_t row_off = static_cast<size_t>(row) * K * kBlockBytes;
-  const uint8_t* wg = a.w + static_cast<size_t>(expert) * a.mat_bytes + row_off;
-  const uint8_t* wu = GU ? a.w_up + static_cast<size_t>(expert) * a.mat_bytes + row_off : nullptr;
+  const int arow = nl & (R2 - 1);
+  // this workgroup's 16 rows of each matrix (rows * K * 144 < 2^31 bytes)
+  const size_t wofs = static_cast<size_t>(expert) * a.mat_bytes +
+                      static_cast<size_t>(n0) * K * kBlockBytes;
+  const uint32_t wbytes = static_cast<uint32_t>(rows) * static_cast<uint32_t>(K) * kBlockBytes;
+  const rsrc_t rg = make_rsrc(a.w + wofs, wbytes);
+  const rsrc_t ru = GU ? make_rsrc(a.w_up + wofs, wbytes) : rg;
+  // activations: offsets are element indices of valid tokens only, so the
+  // resource is left unbounded
+  const rsrc_t rx = make_rsrc(a.x, 0x7FFFFFFFu);
 
   const int kb0 = (wave * K) / kWaves;
   const int kb1 = ((wave + 1) * K) / kWaves;
-  const bool active = nl < mt;  // the A operand token of this lane exists
 
   float yg[4] = {0.f, 0.f, 0.f, 0.f};
   float yu[4] = {0.f, 0.f, 0.f, 0.f};
   WaveLds<MT>& L = lds.wave[wave];
 
-  for (int cb = kb0; cb < kb1; cb += kChunk) {
-    const int nb = min(kChunk, kb1 - cb);
-    // issue every weight load of the chunk before converting activations
-    BlockRegs rg[kChunk], ru[kChunk];
+  for (int cb = kb0; cb < kb1; cb += CH) {
+    const int nb = min(CH, kb1 - cb);
+    // 1. every load of the chunk: activations first (needed first), then
+    //    the weights; lanes past the ends read zeros
+    float4 xv[MT][CH];
 #pragma unroll
-    for (int bi = 0; bi < kChunk; ++bi) {
-      if (bi < nb) {
-        load_block(wg + static_cast<size_t>(cb + bi) * kBlockBytes, g, rg[bi]);
-        if constexpr (GU) load_block(wu + static_cast<size_t>(cb + bi) * kBlockBytes, g, ru[bi]);
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int bi = 0; bi < CH; ++bi) {
+        const uint32_t off = t < mt && bi < nb
+                                 ? static_cast<uint32_t>(xrow[t] * a.ldx + (cb + bi) * kQK + 4 * lane)
+                                 : kOob;
+        xv[t][bi] = load_x4<BF16>(rx, off);
       }
-    }
-    convert_chunk<MT, BF16>(L, a.x, xrow, a.ldx, mt, cb, nb, lane);
-    lds_fence();
+    BlockRegs rgb[CH], rub[GU ? CH : 1];
 #pragma unroll
-    for (int bi = 0; bi < kChunk; ++bi) {
-      if (bi < nb) {
-        const int4 shv = *reinterpret_cast<const int4*>(&L.shift[bi * 16 + 4 * g]);
-        const int shs[4] = {shv.x, shv.y, shv.z, shv.w};
+    for (int bi = 0; bi < CH; ++bi) {
+      const uint32_t off = nl < rows && bi < nb
+                               ? static_cast<uint32_t>(nl * K + cb + bi) * kBlockBytes
+                               : kOob;
+      load_block(rg, off, g, rgb[bi]);
+      if constexpr (GU) load_block(ru, off, g, rub[bi]);
+    }
+    // 2. activations -> operand layout in this wavefront's LDS
+    convert_chunk<MT>(L, xv, mt, nb, lane);
+    lds_fence();
+    // 3. one MFMA chain per block and matrix; C element i of this lane is row
+    //    4g + i: token (4g + i) % HR, hi half when 4g + i < HR, lo when below R2
+#pragma unroll
+    for (int bi = 0; bi < CH; ++bi) {
+      if (bi < nb) {  // uniform
         float d, dmin;
         v4f cm, cn;
-        block_mfma<MT>(rg[bi], g, L, bi, nl, active, d, dmin, cm, cn);
+        int shs[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) shs[i] = L.shift[bi * 8 + ((4 * g + i) & (HR - 1))];
+        block_mfma<MT>(rgb[bi], g, L, bi, arow, d, dmin, cm, cn);
 #pragma unroll
         for (int i = 0; i < 4; ++i) yg[i] += ldexpf(fmaf(d, cm[i], -dmin * cn[i]), -shs[i]);
         if constexpr (GU) {
-          block_mfma<MT>(ru[bi], g, L, bi, nl, active, d, dmin, cm, cn);
+          block_mfma<MT>(rub[bi], g, L, bi, arow, d, dmin, cm, cn);
 #pragma unroll
           for (int i = 0; i < 4; ++i) yu[i] += ldexpf(fmaf(d, cm[i], -dmin * cn[i]), -shs[i]);
         }
@@ -314,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(GemvArgs a) {
   }
 
   __syncthreads();
-  // C layout: lane holds tokens 4g .. 4g+3 of weight row nl
+  // C layout: lane holds rows 4g .. 4g+3 of weight row nl
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     lds.red[0][wave][4 * g + i][nl] = yg[i];
@@ -323,15 +370,16 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(GemvArgs a) {
   __syncthreads();
   const int t = tid / kRows;
   const int r = tid % kRows;
-  if (t < mt && n0 + r < a.n) {
+  if (t < mt && r < rows) {
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += lds.red[0][w][t][r];
+    for (int w = 0; w < kWaves; ++w) s += lds.red[0][w][t][r] + lds.red[0][w][HR + t][r];
     float out = s;
     if constexpr (GU) {
       float su = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) su += lds.red[GU ? 1 : 0][w][t][r];
+      for (int w = 0; w < kWaves; ++w)
+        su += lds.red[GU ? 1 : 0][w][t][r] + lds.red[GU ? 1 : 0][w][HR + t][r];
       out = silu_mul(s, su);
     }
     a.y[static_cast<size_t>(yrow[t]) * a.ldy + n0 + r] = out;
@@ -355,17 +403,11 @@ hipError_t dispatch_m(const GemvArgs& a, hipStream_t stream) {
 
 }  // namespace
 
+// Tokens are rounded up to 4 or 8 (the operand holds hi and lo halves of up
+// to eight tokens either way).
 hipError_t launch_gemv_mfma(const GemvArgs& a, hipStream_t stream) {
-  switch (a.m) {
-    case 1: return dispatch_m<1>(a, stream);
-    case 2: return dispatch_m<2>(a, stream);
-    case 3: return dispatch_m<3>(a, stream);
-    case 4: return dispatch_m<4>(a, stream);
-    case 5: return dispatch_m<5>(a, stream);
-    case 6: return dispatch_m<6>(a, stream);
-    case 7: return dispatch_m<7>(a, stream);
-    default: return dispatch_m<8>(a, stream);
-  }
+  if (a.m <= 4) return dispatch_m<4>(a, stream);
+  return dispatch_m<8>(a, stream);
 }
 
 }  // namespace q4k
