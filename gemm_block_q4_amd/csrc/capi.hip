@@ -25,6 +25,9 @@ constexpr int kMaxDevices = 64;
 constexpr int kDecodeMaxK = 32768;
 // Prefill path: 64 tokens per workgroup row of the grid (grid.y <= 65535).
 constexpr int kPrefillMaxM = 64 * 65535;
+// k bound of the prefill kernels: a workgroup's 128 weight rows and 128
+// activation rows then stay below 2^31 bytes (32-bit buffer offsets).
+constexpr int kPrefillMaxK = 1 << 20;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -191,7 +194,7 @@ int q8_1_quantize(const void* x, int x_dtype, int m, int k, int8_t* qs, uint32_t
 static int mmq_common(const void* w, const int8_t* qs, const uint32_t* ds, float* y,
                       int32_t* partials, int m, int n, int k, void* stream) {
   if (!w || !qs || (!partials && (!ds || !y))) return Q4K_ERR_NULL;
-  if (m < 1 || m > kPrefillMaxM) return Q4K_ERR_SHAPE;
+  if (m < 1 || m > kPrefillMaxM || k > kPrefillMaxK) return Q4K_ERR_SHAPE;
   size_t wbytes;
   int st = check_matrix(n, k, &wbytes);
   if (st) return st;
@@ -253,7 +256,8 @@ int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int
   if (reg == Q4K_REGIME_DECODE && m > Q4K_DECODE_MAX_TOKENS) return Q4K_ERR_SHAPE;
   if (moe && reg != Q4K_REGIME_DECODE) return Q4K_ERR_SHAPE;
   if (reg == Q4K_REGIME_DECODE && (hidden > kDecodeMaxK || inter > kDecodeMaxK)) return Q4K_ERR_SHAPE;
-  if (reg == Q4K_REGIME_PREFILL && m > kPrefillMaxM) return Q4K_ERR_SHAPE;
+  if (reg == Q4K_REGIME_PREFILL && (m > kPrefillMaxM || hidden > kPrefillMaxK || inter > kPrefillMaxK))
+    return Q4K_ERR_SHAPE;
   size_t gu_bytes, dn_bytes;
   int st = check_matrix(inter, hidden, &gu_bytes);
   if (st) return st;

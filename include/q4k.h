@@ -126,7 +126,7 @@ int q8_1_quantize(const void* x, int x_dtype, int m, int k, int8_t* qs, uint32_t
      y[t][j] = sum_b (d*sc)[j][b] * d_a[t][b] * P - (dmin*m)[j][b] * d_a[t][b] * S[t][b]
    w: device block_q4_K [n][k/256]; qs/ds: device Q8_1 of the activations
    [m][k] (as written by q8_1_quantize); y: device f32 [m][n], overwritten.
-   1 <= m <= 64 * 65535, n >= 1, k >= 256, k % 256 == 0.  Integer products are exact
+   1 <= m <= 64 * 65535, n >= 1, 256 <= k <= 2^20, k % 256 == 0.  Integer products are exact
    (int8 MFMA); scales are applied in f32. */
 int q4k_mmq(const void* w, const int8_t* qs, const uint32_t* ds, float* y, int m, int n,
             int k, void* stream);
@@ -160,7 +160,7 @@ size_t ffn_swiglu_q4k_workspace_bytes(int m, int hidden, int inter, int top_k, i
    up in one pass with silu*mul fused); prefill = x -> Q8_1 -> MMQ gate/up
    with fused silu*mul -> h -> Q8_1 -> MMQ down.  MoE needs the decode regime
    (m <= 8).  hidden, inter: multiples of 256 (at most 32768 in the decode
-   regime).
+   regime, at most 2^20 in the prefill regime).
    workspace: device, at least ffn_swiglu_q4k_workspace_bytes(...) bytes.
    Errors: Q4K_ERR_NULL, Q4K_ERR_SHAPE, Q4K_ERR_ALIGN, Q4K_ERR_OVERFLOW,
    Q4K_ERR_WORKSPACE, Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */

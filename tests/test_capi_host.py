@@ -75,6 +75,7 @@ def test_mmq_validation(lib):
     assert lib.q4k_mmq(P, P, P, P, 1, 1, 512 + 32, None) == 2
     assert lib.q4k_mmq(P, P + 1, P, P, 1, 1, 256, None) == 3
     assert lib.q4k_test_mmq_partials(P, P, 1, 1, 256, None, None) == 1
+    assert lib.q4k_mmq(P, P, P, P, 1, 1, (1 << 20) + 256, None) == 2  # k above the prefill limit
 
 
 def test_ffn_validation(lib):
