@@ -32,6 +32,18 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5033.0        # dense int8 MFMA: 256 CU x 2.4 GHz x 8192 ops/clk
 ROTATE_BYTES = 1 << 30         # per rotated tensor set
 
+# HBM bytes of one sweep (the three GEMV launches), measured with rocprofv3 FETCH_SIZE and
+# WRITE_SIZE (each scaled by what it reads for a copy of known size; summary and commands in
+# profiles/gemv_d4_decode_sweep_hbm_traffic.md) for the kernel sources with these SHA-256
+# digests.  Reported only while the sources still match.
+TRAFFIC_SWEEP_BYTES = 61331041
+TRAFFIC_SOURCES = {
+    "gemm_block_q4_amd/csrc/gemv_valu.hip":
+        "7746b7c00c4ed5d86d1ed826f843e71d86a8f726ea0829b0182381385f1895a0",
+    "gemm_block_q4_amd/csrc/q4k_device.hpp":
+        "0ca9cfd803b914df0ad564490c5fd4e9deb5aaf1f4e89c866e6dd71f630d251d",
+}
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -90,6 +102,20 @@ def rotated(tensor_np, total=ROTATE_BYTES, max_copies=None):
         v.copy_(base)
         views.append(v)
     return views
+
+
+def measured_traffic():
+    """TRAFFIC_SWEEP_BYTES if the GEMV sources are the measured ones, else None."""
+    import hashlib
+    for rel, digest in TRAFFIC_SOURCES.items():
+        try:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                data = f.read()
+        except OSError:
+            return None
+        if hashlib.sha256(data).hexdigest() != digest:
+            return None
+    return TRAFFIC_SWEEP_BYTES
 
 
 def timed_graph(fn, steps, warmup):
@@ -281,7 +307,8 @@ def main():
     sum_us = sum(p["us"] for p in per_shape)
     achieved = sum_bytes / (sum_us * 1e-6) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(),
+                    traffic_scope="HBM bytes of the three sweep launches (same scope as achieved)",
                     kernel="gemv_d4_kernel<false, false, 4, true> (q4k_gemv, m=1)",
                     per_shape=[dict(n=p["n"], k=p["k"], us=round(p["us"], 3), gbs=round(p["gbs"], 1))
                                for p in per_shape])
