@@ -309,7 +309,7 @@ def main():
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(),
                     traffic_scope="HBM bytes of the three sweep launches (same scope as achieved)",
-                    kernel="gemv_d4_kernel<false, false, 4, true> (q4k_gemv, m=1)",
+                    kernel="gemv_d4_kernel<false, false, false, 1|2, 1|2, 4> (q4k_gemv, m=1; layout 1 for k=4096, 2 for k=11008)",
                     per_shape=[dict(n=p["n"], k=p["k"], us=round(p["us"], 3), gbs=round(p["gbs"], 1))
                                for p in per_shape])
 

@@ -46,7 +46,6 @@ namespace {
 constexpr int kThreadsMax = 512;
 constexpr int kWavesNarrow = 4;  // wavefronts per workgroup when a row fits one wavefront
 constexpr int kWavesWide = 8;    // at most this many when a row spans wavefronts
-constexpr int kUnitsEarly = 2;  // 16-value activation units per thread loaded before the weights
 constexpr size_t kLdsMax = 160 * 1024;
 
 // Four activations at element offset `off` of a buffer (kOob: zeros).
@@ -63,7 +62,15 @@ __device__ __forceinline__ float4 load_x4(rsrc_t r, uint32_t off) {
   }
 }
 
-// The quarter of one block a lane streams per row.
+// The quarter of one block a lane streams per row.  The four lanes of a
+// block are an aligned lane quad; lane g of the quad loads header word g and
+// the quad shares the four words by DPP broadcasts (one 4-byte load per lane
+// instead of the 16-byte header four times).
+struct RawSlice {
+  uint32_t hw;   // header word g of the block
+  uint4 q0, q1;  // quant bytes 32g .. 32g+31
+};
+
 struct Slice {
   uint32_t h;   // d | dmin << 16
   uint32_t s0;  // scales[0..3]
@@ -73,10 +80,9 @@ struct Slice {
 };
 
 // Slice g of the block at byte offset `off` of the resource (kOob: zeros).
-__device__ __forceinline__ void load_slice(rsrc_t r, uint32_t off, int g, Slice& s) {
-  const uint4 h = buf_load16(r, off);
-  s.h = h.x; s.s0 = h.y; s.s1 = h.z; s.s2 = h.w;
+__device__ __forceinline__ void load_slice(rsrc_t r, uint32_t off, int g, RawSlice& s) {
   const uint32_t q = off + 32u * static_cast<uint32_t>(g);
+  s.hw = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off + 4u * g), 0, 0));
   s.q0 = buf_load16(r, q + 16u);
   s.q1 = buf_load16(r, q + 32u);
 }
@@ -87,6 +93,23 @@ template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
                                                                ROW_MASK, 0xF, true));
+}
+
+// Word i of the lane's quad, in every lane of the quad (quad_perm(i,i,i,i)).
+template <int I>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), I * 0x55, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ Slice expand(const RawSlice& r) {
+  Slice s;
+  s.h = quad_bcast<0>(r.hw);
+  s.s0 = quad_bcast<1>(r.hw);
+  s.s1 = quad_bcast<2>(r.hw);
+  s.s2 = quad_bcast<3>(r.hw);
+  s.q0 = r.q0;
+  s.q1 = r.q1;
+  return s;
 }
 
 // Sum over aligned segments of SEG lanes (SEG a power of two <= 64); the
@@ -186,9 +209,17 @@ __device__ __forceinline__ float slice_dot(const Slice& s, const FieldSel& f, co
 //   wr   = wavefronts per row (1 when lpr <= 64);
 //   rpw  = rows per wavefront per step (64 / lpr when wr == 1, else 1);
 //   step = rows per workgroup per step; rows = rows per workgroup.
+// The kernel divides by none of them: lpr_log = log2(lpr) when wr == 1, and
+// for wr > 1 nibble w of wslot / wpart holds w / wr and w % wr.
 struct Geo {
   int lpr, wr, rpw, waves, step, rows;
+  int lpr_log;
+  uint32_t wslot, wpart;
 };
+
+// Row layouts: rows narrower than a wavefront (segments of lpr lanes), rows of
+// exactly one wavefront, rows spanning wavefronts.
+enum Layout { kNarrow = 0, kOneWave = 1, kWide = 2 };
 
 // LDS words: digit planes [S][48] and slice info [S][4] (scale, sum0, sum1,
 // unused), then the row partials when a row spans wavefronts.
@@ -249,19 +280,26 @@ __device__ __forceinline__ void convert_unit(const float4 (&xr)[4], int u, bool 
   }
 }
 
-template <bool GU, bool BF16, int PF, bool SEG64>
+template <bool GU, bool BF16, bool MOE, int LAYOUT, int XU, int PF>
 __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo geo) {
+  constexpr bool WIDE = LAYOUT == kWide;
+  constexpr bool SEG64 = LAYOUT != kNarrow;
   extern __shared__ __attribute__((aligned(16))) uint32_t smem_u[];
-  const int K = a.k / kQK;
-  const int S = 4 * K;  // slices per row
+  const int K = a.k >> 8;  // blocks per row
+  const int S = 4 * K;     // slices per row
   const int units = 4 * S;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int nthr = geo.waves * 64;
+  // every argument the weight stream needs, fetched in one batch of scalar
+  // loads (otherwise the compiler spreads them over dependent round trips
+  // ahead of the first weight load)
+  asm volatile("" ::"s"(a.w), "s"(a.w_up), "s"(a.x), "s"(a.k), "s"(a.n), "s"(geo.rows), "s"(geo.step),
+               "s"(geo.lpr_log), "s"(geo.wslot), "s"(geo.wpart));
 
   int expert = 0, xrow = 0, yrow = 0;
-  if (a.slot_expert != nullptr) {
+  if constexpr (MOE) {
     const int slot = blockIdx.y;
     expert = a.slot_expert[slot];
     // uniform over the workgroup, before any barrier
@@ -270,25 +308,26 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
     yrow = a.slot_y[slot * kMaxTokens];
   }
 
-  // this lane's row slot and slice
+  // this lane's row slot (within a step) and slice position
   int rslot, slice;
-  if (geo.wr == 1) {
-    rslot = wave * geo.rpw + lane / geo.lpr;
-    slice = lane % geo.lpr;
+  if constexpr (!WIDE) {
+    rslot = wave * geo.rpw + (lane >> geo.lpr_log);
+    slice = lane & ((1 << geo.lpr_log) - 1);
   } else {
-    rslot = wave / geo.wr;
-    slice = (wave % geo.wr) * 64 + lane;
+    rslot = static_cast<int>((geo.wslot >> (4 * wave)) & 15u);
+    slice = static_cast<int>((geo.wpart >> (4 * wave)) & 15u) * 64 + lane;
   }
   const bool lane_ok = slice < S && rslot < geo.step;
   const int b = lane_ok ? slice >> 2 : 0;
-  const int g = slice & 3;
+  const int g = lane & 3;  // == slice & 3: S is a multiple of 4 and segments are aligned
   FieldSel fsel;
   fsel.sh = 8u * static_cast<uint32_t>((2 * g) & 3);
   fsel.upper = g >= 2;
 
+  // step it holds rows it*step .. it*step+step-1 of the workgroup; it exists
+  // while it*step < rows
   const int row0 = blockIdx.x * geo.rows;
   const int rows = min(geo.rows, a.n - row0);
-  const int iters = (rows + geo.step - 1) / geo.step;
 
   // buffer resources: this workgroup's rows of the matrices (under 2^31 bytes
   // by construction of the geometry) and the token's activation row
@@ -300,26 +339,35 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
   const size_t xel = static_cast<size_t>(xrow) * a.ldx;
   const rsrc_t rx = BF16 ? make_rsrc(static_cast<const uint16_t*>(a.x) + xel, 2u * a.k)
                          : make_rsrc(static_cast<const float*>(a.x) + xel, 4u * a.k);
-  // byte offset of this lane's block in row r of the workgroup, kOob past the end
-  auto row_off = [&](int r) -> uint32_t {
-    return lane_ok && r < rows ? static_cast<uint32_t>(r * K + b) * kBlockBytes : kOob;
+  // byte offset of this lane's block in step it: base + it * stride (adds
+  // only), kOob past the last row
+  const uint32_t stride = static_cast<uint32_t>(geo.step * K) * kBlockBytes;
+  const uint32_t base = static_cast<uint32_t>(rslot * K + b) * kBlockBytes;
+  // Products of uniform values go through readfirstlane: the compiler would
+  // otherwise fold them with a lane value into a 64-bit multiply-add whose
+  // (unused) high addend register may be a load still in flight, and wait
+  // for it.
+  auto uni = [](int v) -> int { return __builtin_amdgcn_readfirstlane(v); };
+  auto step_off = [&](int it, uint32_t off) -> uint32_t {
+    return lane_ok && rslot < rows - uni(it * geo.step) ? off : kOob;
   };
   auto unit_off = [&](int u, int c) -> uint32_t {
     return u < units ? static_cast<uint32_t>(16 * u + 4 * c) : kOob;
   };
 
-  // 1. the first activation units of this thread, loaded before any weight
-  float4 xr[kUnitsEarly][4];
+  // 1. this thread's activation units (XU of them, XU * nthr >= units by
+  //    construction of the launch), loaded before any weight
+  float4 xr[XU][4];
 #pragma unroll
-  for (int j = 0; j < kUnitsEarly; ++j)
+  for (int j = 0; j < XU; ++j)
 #pragma unroll
     for (int c = 0; c < 4; ++c) xr[j][c] = load_x4<BF16>(rx, unit_off(tid + j * nthr, c));
 
   // 2. weight loads of the first PF steps
-  Slice sg[PF], su[GU ? PF : 1];
+  RawSlice sg[PF], su[GU ? PF : 1];
 #pragma unroll
   for (int p = 0; p < PF; ++p) {
-    const uint32_t off = row_off(p * geo.step + rslot);
+    const uint32_t off = step_off(p, base + static_cast<uint32_t>(uni(p * static_cast<int>(stride))));
     load_slice(rg, off, g, sg[p]);
     if constexpr (GU) load_slice(ru, off, g, su[p]);
   }
@@ -329,19 +377,14 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
   uint32_t* dig = smem_u;                                                         // [S][48]
   float* xinfo = reinterpret_cast<float*>(smem_u + static_cast<size_t>(S) * 48);  // [S][4]
 #pragma unroll
-  for (int j = 0; j < kUnitsEarly; ++j) {
-    if (j * nthr >= units) break;
+  for (int j = 0; j < XU; ++j) {
     const int u = tid + j * nthr;
     convert_unit(xr[j], u, u < units, dig, xinfo);
   }
-  for (int j = kUnitsEarly; j * nthr < units; ++j) {
-    const int u = tid + j * nthr;
-    float4 xl[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) xl[c] = load_x4<BF16>(rx, unit_off(u, c));
-    convert_unit(xl, u, u < units, dig, xinfo);
-  }
-  __syncthreads();
+  // A barrier without a memory fence: the digits are LDS writes, complete at
+  // lgkmcnt(0), and a fence would also wait for the weight loads in flight.
+  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
   XSlice xs;
   {
     const uint32_t* base = dig + static_cast<size_t>(lane_ok ? slice : 0) * 48;
@@ -358,73 +401,67 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
   }
 
   // 4. row loop: consume step p while steps p+1 .. p+PF-1 are in flight.  The
-  //    loads are never under a branch (rows past the end read kOob); inactive
-  //    lanes contribute 0 to the DPP segment sums.
+  //    loads are never under a branch (rows past the end read kOob), the last
+  //    group issues none, and inactive lanes contribute 0 to the DPP sums.
   float* part = reinterpret_cast<float*>(smem_u + x_words(S));  // [GU?2:1][rows][wr]
-  const int seg = SEG64 ? 64 : (geo.wr == 1 ? geo.lpr : 64);
+  const int seg_mask = SEG64 ? 63 : (1 << geo.lpr_log) - 1;
+  auto dot = [&](const RawSlice& raw, bool ok) -> float {
+    const float v = slice_dot(expand(raw), fsel, xs);
+    return ok ? v : 0.f;
+  };
   auto finish = [&](float (&o)[PF], float (&ou)[PF], int it0) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      o[p] = SEG64 ? segment_sum<64>(o[p]) : segment_sum_rt(o[p], seg);
-      if constexpr (GU) ou[p] = SEG64 ? segment_sum<64>(ou[p]) : segment_sum_rt(ou[p], seg);
+      o[p] = SEG64 ? segment_sum<64>(o[p]) : segment_sum_rt(o[p], seg_mask + 1);
+      if constexpr (GU) ou[p] = SEG64 ? segment_sum<64>(ou[p]) : segment_sum_rt(ou[p], seg_mask + 1);
     }
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      const int it = it0 + p;
-      const int r = it * geo.step + rslot;
+      const int r = uni((it0 + p) * geo.step) + rslot;
       // the segment's last lane holds the row sum (it may be a padding lane)
-      if (it < iters && rslot < geo.step && r < rows && (lane % seg) == seg - 1) {
-        if (geo.wr == 1) {
+      if (rslot < geo.step && r < rows && (lane & seg_mask) == seg_mask) {
+        if constexpr (!WIDE) {
           float out = o[p];
           if constexpr (GU) out = silu_mul(o[p], ou[p]);
           a.y[static_cast<size_t>(yrow) * a.ldy + row0 + r] = out;
         } else {
-          part[r * geo.wr + slice / 64] = o[p];
-          if constexpr (GU) part[(rows + r) * geo.wr + slice / 64] = ou[p];
+          part[r * geo.wr + (slice >> 6)] = o[p];
+          if constexpr (GU) part[(rows + r) * geo.wr + (slice >> 6)] = ou[p];
         }
       }
     }
   };
   int it0 = 0;
-  for (; it0 + PF <= iters; it0 += PF) {
+  uint32_t next = base + PF * stride;  // offset of step it0 + PF
+  for (; (it0 + PF) * geo.step < rows; it0 += PF, next += PF * stride) {  // uniform; a later group exists
     float o[PF], ou[PF];
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      const int r = (it0 + p) * geo.step + rslot;
-      const bool ok = lane_ok && r < rows;
-      const float v = slice_dot(sg[p], fsel, xs);
-      o[p] = ok ? v : 0.f;
+      const bool ok = lane_ok && rslot < rows - uni((it0 + p) * geo.step);
+      o[p] = dot(sg[p], ok);
       ou[p] = 0.f;
-      if constexpr (GU) {
-        const float vu = slice_dot(su[p], fsel, xs);
-        ou[p] = ok ? vu : 0.f;
-      }
-      const uint32_t off = row_off((it0 + p + PF) * geo.step + rslot);
+      if constexpr (GU) ou[p] = dot(su[p], ok);
+      const uint32_t off = step_off(it0 + p + PF, next + static_cast<uint32_t>(uni(p * static_cast<int>(stride))));
       load_slice(rg, off, g, sg[p]);
       if constexpr (GU) load_slice(ru, off, g, su[p]);
     }
     finish(o, ou, it0);
   }
-  if (it0 < iters) {  // the last, partial group: nothing left to prefetch
+  {  // the last group: nothing left to load
     float o[PF], ou[PF];
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
       o[p] = 0.f;
       ou[p] = 0.f;
-      if (it0 + p < iters) {  // uniform
-        const int r = (it0 + p) * geo.step + rslot;
-        const bool ok = lane_ok && r < rows;
-        const float v = slice_dot(sg[p], fsel, xs);
-        o[p] = ok ? v : 0.f;
-        if constexpr (GU) {
-          const float vu = slice_dot(su[p], fsel, xs);
-          ou[p] = ok ? vu : 0.f;
-        }
+      if ((it0 + p) * geo.step < rows) {  // uniform
+        const bool ok = lane_ok && rslot < rows - uni((it0 + p) * geo.step);
+        o[p] = dot(sg[p], ok);
+        if constexpr (GU) ou[p] = dot(su[p], ok);
       }
     }
     finish(o, ou, it0);
   }
-  if (geo.wr == 1) return;  // uniform: no wavefront of this workgroup waits below
+  if constexpr (!WIDE) return;
   __syncthreads();
   // 5. rows that span wavefronts: add the per-wavefront sums in order
   for (int r = tid; r < rows; r += nthr) {
@@ -451,7 +488,11 @@ Geo make_geo(int n, int k, int slots, bool gu) {
   const int l = 4 * K;
   if (l <= 64) {
     g.lpr = 1;
-    while (g.lpr < l) g.lpr <<= 1;
+    g.lpr_log = 0;
+    while (g.lpr < l) {
+      g.lpr <<= 1;
+      ++g.lpr_log;
+    }
     g.wr = 1;
     g.rpw = 64 / g.lpr;
     g.waves = kWavesNarrow;
@@ -462,6 +503,10 @@ Geo make_geo(int n, int k, int slots, bool gu) {
     g.rpw = 1;
     g.waves = g.wr * (g.wr >= kWavesWide ? 1 : kWavesWide / g.wr);  // whole rows
     g.step = g.waves / g.wr;
+    for (int w = 0; w < g.waves; ++w) {  // waves <= 8: one nibble each
+      g.wslot |= static_cast<uint32_t>(w / g.wr) << (4 * w);
+      g.wpart |= static_cast<uint32_t>(w % g.wr) << (4 * w);
+    }
   }
   // rows per workgroup: about 256 workgroups over all slots, whole steps,
   // and no more row partials than fit next to the digits in LDS
@@ -480,29 +525,48 @@ Geo make_geo(int n, int k, int slots, bool gu) {
   return g;
 }
 
-template <bool GU, bool BF16>
-hipError_t launch_d4(const GemvArgs& a, hipStream_t stream) {
+template <bool GU, bool BF16, bool MOE, int LAYOUT, int XU>
+hipError_t launch_layout(const GemvArgs& a, const Geo& geo, size_t lds, hipStream_t stream) {
   constexpr int PF = GU ? 2 : 4;
-  const int slots = a.slot_expert ? a.slots : 1;
-  const Geo geo = make_geo(a.n, a.k, slots, GU);
-  const size_t lds = lds_bytes(geo, a.k, GU);
-  if (geo.rows < geo.step || lds > kLdsMax) return hipErrorInvalidValue;
-  // rows of exactly one wavefront reduce over all 64 lanes
-  const bool seg64 = geo.wr > 1 || geo.lpr == 64;
-  auto kern = seg64 ? gemv_d4_kernel<GU, BF16, PF, true> : gemv_d4_kernel<GU, BF16, PF, false>;
+  auto kern = gemv_d4_kernel<GU, BF16, MOE, LAYOUT, XU, PF>;
   static bool big_lds = false;  // the opt-in is per kernel and stays set
   if (lds > 64 * 1024 && !big_lds) {
-    for (auto kv : {gemv_d4_kernel<GU, BF16, PF, true>, gemv_d4_kernel<GU, BF16, PF, false>}) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kv),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               static_cast<int>(kLdsMax));
-      if (e != hipSuccess) return e;
-    }
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(kLdsMax));
+    if (e != hipSuccess) return e;
     big_lds = true;
   }
+  const int slots = MOE ? a.slots : 1;
   const dim3 grid((a.n + geo.rows - 1) / geo.rows, slots);
   kern<<<grid, dim3(geo.waves * 64), lds, stream>>>(a, geo);
   return hipGetLastError();
+}
+
+template <bool GU, bool BF16, bool MOE>
+hipError_t launch_moe(const GemvArgs& a, hipStream_t stream) {
+  const int slots = MOE ? a.slots : 1;
+  const Geo geo = make_geo(a.n, a.k, slots, GU);
+  const size_t lds = lds_bytes(geo, a.k, GU);
+  if (geo.rows < geo.step || lds > kLdsMax) return hipErrorInvalidValue;
+  // activation units (16 values) per thread: one when a row fits a wavefront
+  // (at most 256 units for 256 threads), else two or four (k <= 32768 keeps
+  // units <= 4 * threads for every row width)
+  const int units = 16 * (a.k / kQK);
+  const int nthr = geo.waves * 64;
+  if (geo.wr > 1) {
+    if (units <= 2 * nthr) return launch_layout<GU, BF16, MOE, kWide, 2>(a, geo, lds, stream);
+    if (units <= 4 * nthr) return launch_layout<GU, BF16, MOE, kWide, 4>(a, geo, lds, stream);
+    return hipErrorInvalidValue;
+  }
+  if (units > nthr) return hipErrorInvalidValue;
+  if (geo.lpr == 64) return launch_layout<GU, BF16, MOE, kOneWave, 1>(a, geo, lds, stream);
+  return launch_layout<GU, BF16, MOE, kNarrow, 1>(a, geo, lds, stream);
+}
+
+template <bool GU, bool BF16>
+hipError_t launch_d4(const GemvArgs& a, hipStream_t stream) {
+  return a.slot_expert ? launch_moe<GU, BF16, true>(a, stream) : launch_moe<GU, BF16, false>(a, stream);
 }
 
 }  // namespace
