@@ -36,10 +36,10 @@ ROTATE_BYTES = 1 << 30         # per rotated tensor set
 # WRITE_SIZE (each scaled by what it reads for a copy of known size; summary and commands in
 # profiles/gemv_d4_decode_sweep_hbm_traffic.md) for the kernel sources with these SHA-256
 # digests.  Reported only while the sources still match.
-TRAFFIC_SWEEP_BYTES = 61331041
+TRAFFIC_SWEEP_BYTES = 61267597
 TRAFFIC_SOURCES = {
     "gemm_block_q4_amd/csrc/gemv_valu.hip":
-        "7746b7c00c4ed5d86d1ed826f843e71d86a8f726ea0829b0182381385f1895a0",
+        "bfaff7adac514b16bd5ceb2c8b89c5f1035d8657257f504812cbd096ac1cf71e",
     "gemm_block_q4_amd/csrc/q4k_device.hpp":
         "0ca9cfd803b914df0ad564490c5fd4e9deb5aaf1f4e89c866e6dd71f630d251d",
 }
