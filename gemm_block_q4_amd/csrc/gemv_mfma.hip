@@ -11,17 +11,18 @@
 //  * weights: for sub-block j the product sc_j * q is an integer <= 945,
 //    exact in binary16, so each 256-block is one chain of 8 K=32 steps whose
 //    f32 sum is multiplied by d once; the min term sum_j m_j * X_j (X_j the
-//    activation sum of sub-block j, carried as X_j * 2^-6 against m_j * 2^6
-//    so that it fits binary16) is one more K=32 step whose result is
-//    multiplied by dmin;
-//  * activations: per token and 256-block, x is scaled by 2^sh (sh chosen so
-//    the block maximum lands in [2^14, 2^15)) and split into two binary16
-//    halves hi + lo that carry 22 significant bits.  The 16 rows of the
-//    activation operand hold the hi halves of tokens 0..7 (rows 0..7) and the
-//    lo halves (rows 8..15), so one MFMA per step multiplies both halves of
-//    every token by the same weight operand; the two result rows of a token
-//    are added at the end.
-// The relative error of a row result is thus a few 2^-22 of ||w|| ||x||.
+//    activation sum of sub-block j) is a second chain over the same
+//    activation operand with m_j (<= 63, exact) as the weight operand, its
+//    sum multiplied by dmin;
+//  * activations: per token and chunk of blocks, x is scaled by 2^sh (sh
+//    chosen so the chunk maximum lands in [2^14, 2^15)) and split into two
+//    binary16 halves: hi = x rounded toward zero, lo = (x - hi) rounded
+//    toward zero (x - hi is exact in f32), together 21 significant bits or
+//    more.  The 16 rows of the activation operand hold the hi halves of
+//    tokens 0..7 (rows 0..7) and the lo halves (rows 8..15), so one MFMA per
+//    step multiplies both halves of every token by the same weight operand;
+//    the two result rows of a token are added at the end.
+// The relative error of a row result is thus a few 2^-21 of ||w|| ||x||.
 //
 // Work decomposition: a workgroup (4 wavefronts) owns 16 output rows; the
 // k/256 blocks are split into four contiguous ranges, one per wavefront.
@@ -58,15 +59,13 @@ template <int MT> constexpr int chunk_blocks() { return MT <= 4 ? 4 : 2; }
 // LDS of one wavefront's activation operands for a chunk, R2 = 2 * half_rows:
 //   op: [CH][8 steps][4 lane groups][R2 rows] x 8 halves (16 B per entry);
 //       rows 0..HR-1 hold the hi halves of the tokens, rows HR..R2-1 the lo
-//   xs: [CH][4 lane groups][R2 rows] two halves (X_{2g}, X_{2g+1}) * 2^-6
-//   shift: [CH][8] exponent sh per token
+//   shift: [8] exponent sh per token (one per chunk)
 template <int MT>
 struct WaveLds {
   static constexpr int kCH = chunk_blocks<MT>();
   static constexpr int kR2 = 2 * half_rows<MT>();
   uint4 op[kCH * 8 * 4 * kR2];
-  uint32_t xs[kCH * 4 * kR2];
-  int shift[kCH * 8];
+  int shift[8];
 };
 
 template <int MT, bool GU>
@@ -92,11 +91,6 @@ __device__ __forceinline__ float4 load_x4(rsrc_t r, uint32_t off) {
   }
 }
 
-__device__ __forceinline__ uint32_t pack_half2(_Float16 a, _Float16 b) {
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
-}
-
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
@@ -115,25 +109,32 @@ __device__ __forceinline__ float wave_max_nonneg(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
-// Exponent that maps a block maximum into [2^14, 2^15) (0 for an all-zero
-// block).
+// Exponent that maps a maximum |x| into [2^14, 2^15) (0 when all values are
+// zero).
 __device__ __forceinline__ int block_shift(float amax) {
   const int eb = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu);
   return amax > 0.0f ? 141 - eb : 0;
 }
 
-// v = hi + lo with binary16 halves, to 22 significant bits.
-__device__ __forceinline__ void split_half(float v, _Float16& hi, _Float16& lo) {
-  hi = static_cast<_Float16>(v);
-  lo = static_cast<_Float16>(v - static_cast<float>(hi));
-}
-
 // Converts loaded activations of one chunk into operand layout.  Lane l owns
 // values 4l .. 4l+3 of each 256-block: operand step s = (l % 16) / 2, lane
-// group g = l / 16, halves 4*(l%2) .. +3, sub-block j = l / 8.  Tokens at or
-// past the live count `mt` and blocks past `nb` are skipped (uniform branches):
-// their operand rows hold stale values, which only reach result rows that are
-// never read.
+// group g = l / 16, halves 4*(l%2) .. +3.  One scale per token for the whole
+// chunk (blocks past `nb` were loaded as zeros and do not move the maximum).
+// Tokens at or past the live count `mt` and blocks past `nb` are skipped
+// (uniform branches): their operand rows hold stale values, which only reach
+// result rows that are never read.
+__device__ __forceinline__ uint32_t pkrtz(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+
+__device__ __forceinline__ float lo_half(uint32_t v) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v & 0xFFFFu)));
+}
+
+__device__ __forceinline__ float hi_half(uint32_t v) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v >> 16)));
+}
+
 template <int MT>
 __device__ __forceinline__ void convert_chunk(WaveLds<MT>& L, const float4 (&xv)[MT][WaveLds<MT>::kCH],
                                               int mt, int nb, int lane) {
@@ -144,43 +145,30 @@ __device__ __forceinline__ void convert_chunk(WaveLds<MT>& L, const float4 (&xv)
   const int g = lane >> 4;
   const int half = lane & 1;
 #pragma unroll
-  for (int bi = 0; bi < CH; ++bi) {
-    if (bi >= nb) break;
+  for (int t = 0; t < MT; ++t) {
+    if (t >= mt) break;
+    float amax = 0.f;
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      if (t >= mt) break;
+    for (int bi = 0; bi < CH; ++bi) {
       const float4 v = xv[t][bi];
-      float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-      amax = wave_max_nonneg(amax);
-      const int sh = block_shift(amax);
-      const float v0 = ldexpf(v.x, sh), v1 = ldexpf(v.y, sh);
-      const float v2 = ldexpf(v.z, sh), v3 = ldexpf(v.w, sh);
-      _Float16 h0, h1, h2, h3, l0, l1, l2, l3;
-      split_half(v0, h0, l0);
-      split_half(v1, h1, l1);
-      split_half(v2, h2, l2);
-      split_half(v3, h3, l3);
-      const int e = ((bi * 8 + s) * 4 + g) * R2 + t;
-      reinterpret_cast<uint2*>(&L.op[e])[half] = make_uint2(pack_half2(h0, h1), pack_half2(h2, h3));
-      reinterpret_cast<uint2*>(&L.op[e + HR])[half] = make_uint2(pack_half2(l0, l1), pack_half2(l2, l3));
-      // sum of the scaled values of sub-block j = lane / 8 (an aligned octet
-      // of one DPP row): lanes 8j+4 .. 8j+7 end with the octet's sum
-      float xs = (v0 + v1) + (v2 + v3);
-      xs += dpp<0xB1>(xs);
-      xs += dpp<0x4E>(xs);
-      xs += dpp<0x114>(xs);
-      if ((lane & 7) == 7) {
-        const int j = lane >> 3;  // sub-block: lane group j/2, K slot j%2
-        // |xs| < 32 * 2^15; the sum is stored as xs * 2^-6 (the mins are
-        // used as m * 2^6 <= 4032, still exact) to stay inside binary16
-        _Float16 xh, xl;
-        split_half(xs * 0.015625f, xh, xl);
-        const int ei = (bi * 4 + (j >> 1)) * R2 + t;
-        reinterpret_cast<uint16_t*>(&L.xs[ei])[j & 1] = __builtin_bit_cast(uint16_t, xh);
-        reinterpret_cast<uint16_t*>(&L.xs[ei + HR])[j & 1] = __builtin_bit_cast(uint16_t, xl);
-      }
-      if (lane == 0) L.shift[bi * 8 + t] = sh;
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     }
+    amax = wave_max_nonneg(amax);
+    const int sh = block_shift(amax);
+#pragma unroll
+    for (int bi = 0; bi < CH; ++bi) {
+      if (bi >= nb) break;
+      const float4 x = xv[t][bi];
+      const float v0 = ldexpf(x.x, sh), v1 = ldexpf(x.y, sh);
+      const float v2 = ldexpf(x.z, sh), v3 = ldexpf(x.w, sh);
+      const uint32_t h01 = pkrtz(v0, v1), h23 = pkrtz(v2, v3);
+      const uint32_t l01 = pkrtz(v0 - lo_half(h01), v1 - hi_half(h01));
+      const uint32_t l23 = pkrtz(v2 - lo_half(h23), v3 - hi_half(h23));
+      const int e = ((bi * 8 + s) * 4 + g) * R2 + t;
+      reinterpret_cast<uint2*>(&L.op[e])[half] = make_uint2(h01, h23);
+      reinterpret_cast<uint2*>(&L.op[e + HR])[half] = make_uint2(l01, l23);
+    }
+    if (lane == 0) L.shift[t] = sh;
   }
 }
 
@@ -232,22 +220,22 @@ __device__ __forceinline__ void block_mfma(const BlockRegs& r, int g, const Wave
   const v2h s0 = v2h{fs0, fs0}, o0 = v2h{fo0, fo0};
   const v2h s1 = v2h{fs1, fs1}, o1 = v2h{fo1, fo1};
   const uint32_t w[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
+  // min term: the K values of lane group g in steps 0..3 belong to sub-block
+  // 2g, in steps 4..7 to sub-block 2g+1
+  const _Float16 fm0 = static_cast<_Float16>(static_cast<float>(mn0));
+  const _Float16 fm1 = static_cast<_Float16>(static_cast<float>(mn1));
+  const v8h bm0 = v8h{fm0, fm0, fm0, fm0, fm0, fm0, fm0, fm0};
+  const v8h bm1 = v8h{fm1, fm1, fm1, fm1, fm1, fm1, fm1, fm1};
   cm = v4f{0.f, 0.f, 0.f, 0.f};
+  cn = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
     const v8h b = s < 4 ? weights8(w[2 * s], w[2 * s + 1], s0, o0)
                         : weights8(w[2 * (s - 4)] >> 4, w[2 * (s - 4) + 1] >> 4, s1, o1);
     const v8h av = __builtin_bit_cast(v8h, L.op[((bi * 8 + s) * 4 + g) * R2 + arow]);
     cm = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b, cm, 0, 0, 0);
+    cn = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, s < 4 ? bm0 : bm1, cn, 0, 0, 0);
   }
-  // min term: K slots 0 and 1 of lane group g hold (m_{2g}, m_{2g+1}) and the
-  // activation sums (X_{2g}, X_{2g+1}); the other slots are zero
-  const v8h bm = v8h{static_cast<_Float16>(64.0f * static_cast<float>(mn0)),
-                     static_cast<_Float16>(64.0f * static_cast<float>(mn1)), 0, 0, 0, 0, 0, 0};
-  const v2h px = __builtin_bit_cast(v2h, L.xs[(bi * 4 + g) * R2 + arow]);
-  const v8h xm = v8h{px[0], px[1], 0, 0, 0, 0, 0, 0};
-  cn = v4f{0.f, 0.f, 0.f, 0.f};
-  cn = __builtin_amdgcn_mfma_f32_16x16x32_f16(xm, bm, cn, 0, 0, 0);
 }
 
 __device__ __forceinline__ void lds_fence() {
@@ -346,7 +334,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(GemvArgs a) {
         v4f cm, cn;
         int shs[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) shs[i] = L.shift[bi * 8 + ((4 * g + i) & (HR - 1))];
+        for (int i = 0; i < 4; ++i) shs[i] = L.shift[(4 * g + i) & (HR - 1)];
         block_mfma<MT>(rgb[bi], g, L, bi, arow, d, dmin, cm, cn);
 #pragma unroll
         for (int i = 0; i < 4; ++i) yg[i] += ldexpf(fmaf(d, cm[i], -dmin * cn[i]), -shs[i]);
