@@ -24,8 +24,9 @@
 //    the two result rows of a token are added at the end.
 // The relative error of a row result is thus a few 2^-21 of ||w|| ||x||.
 //
-// Work decomposition: a workgroup (4 wavefronts) owns 16 output rows; the
-// k/256 blocks are split into four contiguous ranges, one per wavefront.
+// Work decomposition: a workgroup (W = 4 or 8 wavefronts) owns 16 output
+// rows; the k/256 blocks are split into W contiguous ranges, one per
+// wavefront.
 // Lane l holds weight row n0 + l%16 and the 64 weights 64*(l/16) .. +63 of
 // each block (32 contiguous quant bytes, two 16-byte loads), i.e. the K
 // index 8*(l/16)+i of step s is weight 64*(l/16) + 8*s + i; the activation
@@ -33,8 +34,8 @@
 // activation range a chunk of blocks at a time into LDS in operand layout.
 // Every global load is a raw buffer load (out-of-range lanes read zero), all
 // loads of a chunk are issued before any of them is used, and reductions
-// across lanes use DPP, so a chunk costs one memory latency.  The four
-// partial tiles are added in a fixed order at the end (deterministic).
+// across lanes use DPP, so a chunk costs one memory latency.  The W partial
+// tiles are added in a fixed order at the end (deterministic).
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
 
@@ -46,8 +47,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
+constexpr int kWavesMax = 8;  // wavefronts per workgroup: 4, or 8 when the workgroups fit the CUs
 constexpr int kRows = 16;  // output rows per workgroup (MFMA N)
 
 // Tokens per half of the activation operand (4 or 8), and blocks converted
@@ -68,11 +68,11 @@ struct WaveLds {
   int shift[8];
 };
 
-template <int MT, bool GU>
+template <int MT, bool GU, int W>
 struct Lds {
   union {
-    WaveLds<MT> wave[kWaves];
-    float red[GU ? 2 : 1][kWaves][16][kRows];
+    WaveLds<MT> wave[W];
+    float red[GU ? 2 : 1][W][16][kRows];
   };
 };
 
@@ -245,12 +245,12 @@ __device__ __forceinline__ void lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-template <int MT, bool GU, bool BF16>
-__global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(GemvArgs a) {
+template <int MT, bool GU, bool BF16, int W>
+__global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(GemvArgs a) {
   constexpr int CH = WaveLds<MT>::kCH;
   constexpr int R2 = WaveLds<MT>::kR2;
   constexpr int HR = R2 / 2;
-  __shared__ Lds<MT, GU> lds;
+  __shared__ Lds<MT, GU, W> lds;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -292,8 +292,8 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(GemvArgs a) {
   // resource is left unbounded
   const rsrc_t rx = make_rsrc(a.x, 0x7FFFFFFFu);
 
-  const int kb0 = (wave * K) / kWaves;
-  const int kb1 = ((wave + 1) * K) / kWaves;
+  const int kb0 = (wave * K) / W;
+  const int kb1 = ((wave + 1) * K) / W;
 
   float yg[4] = {0.f, 0.f, 0.f, 0.f};
   float yu[4] = {0.f, 0.f, 0.f, 0.f};
@@ -361,12 +361,12 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(GemvArgs a) {
   if (t < mt && r < rows) {
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += lds.red[0][w][t][r] + lds.red[0][w][HR + t][r];
+    for (int w = 0; w < W; ++w) s += lds.red[0][w][t][r] + lds.red[0][w][HR + t][r];
     float out = s;
     if constexpr (GU) {
       float su = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w)
+      for (int w = 0; w < W; ++w)
         su += lds.red[GU ? 1 : 0][w][t][r] + lds.red[GU ? 1 : 0][w][HR + t][r];
       out = silu_mul(s, su);
     }
@@ -374,19 +374,29 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(GemvArgs a) {
   }
 }
 
-template <int MT>
-hipError_t dispatch_m(const GemvArgs& a, hipStream_t stream) {
-  const dim3 grid((a.n + kRows - 1) / kRows, a.slot_expert ? a.slots : 1);
+template <int MT, int W>
+hipError_t dispatch_w(const GemvArgs& a, const dim3& grid, hipStream_t stream) {
   const bool gu = a.w_up != nullptr;
   const bool bf = a.x_bf16 != 0;
   if (gu) {
-    if (bf) gemv_mfma_kernel<MT, true, true><<<grid, dim3(kThreads), 0, stream>>>(a);
-    else gemv_mfma_kernel<MT, true, false><<<grid, dim3(kThreads), 0, stream>>>(a);
+    if (bf) gemv_mfma_kernel<MT, true, true, W><<<grid, dim3(64 * W), 0, stream>>>(a);
+    else gemv_mfma_kernel<MT, true, false, W><<<grid, dim3(64 * W), 0, stream>>>(a);
   } else {
-    if (bf) gemv_mfma_kernel<MT, false, true><<<grid, dim3(kThreads), 0, stream>>>(a);
-    else gemv_mfma_kernel<MT, false, false><<<grid, dim3(kThreads), 0, stream>>>(a);
+    if (bf) gemv_mfma_kernel<MT, false, true, W><<<grid, dim3(64 * W), 0, stream>>>(a);
+    else gemv_mfma_kernel<MT, false, false, W><<<grid, dim3(64 * W), 0, stream>>>(a);
   }
   return hipGetLastError();
+}
+
+// k is split over the wavefronts of a workgroup.  Eight wavefronts (two per
+// SIMD, so that one converts or multiplies while the other waits on memory)
+// need 128 KiB of LDS, one workgroup per CU: they pay off while all
+// workgroups fit on the 256 CUs at once, four wavefronts otherwise.
+template <int MT>
+hipError_t dispatch_m(const GemvArgs& a, hipStream_t stream) {
+  const dim3 grid((a.n + kRows - 1) / kRows, a.slot_expert ? a.slots : 1);
+  if (static_cast<long long>(grid.x) * grid.y <= 256) return dispatch_w<MT, kWavesMax>(a, grid, stream);
+  return dispatch_w<MT, 4>(a, grid, stream);
 }
 
 }  // namespace
