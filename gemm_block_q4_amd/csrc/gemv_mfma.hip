@@ -24,9 +24,9 @@
 //    the two result rows of a token are added at the end.
 // The relative error of a row result is thus a few 2^-21 of ||w|| ||x||.
 //
-// Work decomposition: a workgroup (W = 4 or 8 wavefronts) owns 16 output
-// rows; the k/256 blocks are split into W contiguous ranges, one per
-// wavefront.
+// Work decomposition: a workgroup (W = 4 or 8 wavefronts) owns RT tiles of
+// 16 output rows; the k/256 blocks are split into W contiguous ranges, one
+// per wavefront.
 // Lane l holds weight row n0 + l%16 and the 64 weights 64*(l/16) .. +63 of
 // each block (32 contiguous quant bytes, two 16-byte loads), i.e. the K
 // index 8*(l/16)+i of step s is weight 64*(l/16) + 8*s + i; the activation
@@ -36,6 +36,8 @@
 // loads of a chunk are issued before any of them is used, and reductions
 // across lanes use DPP, so a chunk costs one memory latency.  The W partial
 // tiles are added in a fixed order at the end (deterministic).
+#include <type_traits>
+
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
 
@@ -77,18 +79,33 @@ struct Lds {
 };
 
 // Four activations at element offset `off` of the activation buffer (kOob:
-// zeros).
+// zeros), kept as loaded (bf16 pairs stay packed, half the registers) until
+// the conversion widens them.
 template <bool BF16>
-__device__ __forceinline__ float4 load_x4(rsrc_t r, uint32_t off) {
+struct XRaw {
+  using type = float4;
+};
+template <>
+struct XRaw<true> {
+  using type = uint2;
+};
+
+template <bool BF16>
+__device__ __forceinline__ typename XRaw<BF16>::type load_x4(rsrc_t r, uint32_t off) {
   if constexpr (BF16) {
-    const uint2 raw = buf_load8(r, off == kOob ? kOob : 2u * off);
-    return make_float4(bf16_bits_to_float(raw.x & 0xFFFFu), bf16_bits_to_float(raw.x >> 16),
-                       bf16_bits_to_float(raw.y & 0xFFFFu), bf16_bits_to_float(raw.y >> 16));
+    return buf_load8(r, off == kOob ? kOob : 2u * off);
   } else {
     const uint4 raw = buf_load16(r, off == kOob ? kOob : 4u * off);
     return make_float4(__uint_as_float(raw.x), __uint_as_float(raw.y), __uint_as_float(raw.z),
                        __uint_as_float(raw.w));
   }
+}
+
+__device__ __forceinline__ float4 widen(const float4& v) { return v; }
+
+__device__ __forceinline__ float4 widen(const uint2& raw) {
+  return make_float4(bf16_bits_to_float(raw.x & 0xFFFFu), bf16_bits_to_float(raw.x >> 16),
+                     bf16_bits_to_float(raw.y & 0xFFFFu), bf16_bits_to_float(raw.y >> 16));
 }
 
 template <int CTRL, int ROW_MASK = 0xF>
@@ -135,8 +152,8 @@ __device__ __forceinline__ float hi_half(uint32_t v) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v >> 16)));
 }
 
-template <int MT>
-__device__ __forceinline__ void convert_chunk(WaveLds<MT>& L, const float4 (&xv)[MT][WaveLds<MT>::kCH],
+template <int MT, typename XT>
+__device__ __forceinline__ void convert_chunk(WaveLds<MT>& L, const XT (&xv)[MT][WaveLds<MT>::kCH],
                                               int mt, int nb, int lane) {
   constexpr int CH = WaveLds<MT>::kCH;
   constexpr int R2 = WaveLds<MT>::kR2;
@@ -150,7 +167,7 @@ __device__ __forceinline__ void convert_chunk(WaveLds<MT>& L, const float4 (&xv)
     float amax = 0.f;
 #pragma unroll
     for (int bi = 0; bi < CH; ++bi) {
-      const float4 v = xv[t][bi];
+      const float4 v = widen(xv[t][bi]);
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     }
     amax = wave_max_nonneg(amax);
@@ -158,7 +175,7 @@ __device__ __forceinline__ void convert_chunk(WaveLds<MT>& L, const float4 (&xv)
 #pragma unroll
     for (int bi = 0; bi < CH; ++bi) {
       if (bi >= nb) break;
-      const float4 x = xv[t][bi];
+      const float4 x = widen(xv[t][bi]);
       const float v0 = ldexpf(x.x, sh), v1 = ldexpf(x.y, sh);
       const float v2 = ldexpf(x.z, sh), v3 = ldexpf(x.w, sh);
       const uint32_t h01 = pkrtz(v0, v1), h23 = pkrtz(v2, v3);
@@ -245,7 +262,7 @@ __device__ __forceinline__ void lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-template <int MT, bool GU, bool BF16, int W>
+template <int MT, bool GU, bool BF16, int W, int RT>
 __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(GemvArgs a) {
   constexpr int CH = WaveLds<MT>::kCH;
   constexpr int R2 = WaveLds<MT>::kR2;
@@ -253,7 +270,10 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(GemvArgs a) {
   __shared__ Lds<MT, GU, W> lds;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // uniform in the wavefront; readfirstlane tells the compiler so, which keeps
+  // the chunk loop's branches scalar (a vector branch around a load makes the
+  // compiler wait for it at the join)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = a.k / kQK;
 
   int expert = 0, mt = a.m;
@@ -277,12 +297,13 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(GemvArgs a) {
     }
   }
 
-  const int n0 = blockIdx.x * kRows;
-  const int rows = min(kRows, a.n - n0);
+  // this workgroup's RT tiles of 16 rows
+  const int n0 = blockIdx.x * (RT * kRows);
+  const int rows = min(RT * kRows, a.n - n0);
   const int nl = lane & 15;   // B operand weight row / A operand row / C column
   const int g = lane >> 4;    // lane group: K slots 8g .. 8g+7
   const int arow = nl & (R2 - 1);
-  // this workgroup's 16 rows of each matrix (rows * K * 144 < 2^31 bytes)
+  // the workgroup's rows of each matrix (at most 48 rows * 128 blocks * 144 bytes)
   const size_t wofs = static_cast<size_t>(expert) * a.mat_bytes +
                       static_cast<size_t>(n0) * K * kBlockBytes;
   const uint32_t wbytes = static_cast<uint32_t>(rows) * static_cast<uint32_t>(K) * kBlockBytes;
@@ -295,108 +316,162 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(GemvArgs a) {
   const int kb0 = (wave * K) / W;
   const int kb1 = ((wave + 1) * K) / W;
 
-  float yg[4] = {0.f, 0.f, 0.f, 0.f};
-  float yu[4] = {0.f, 0.f, 0.f, 0.f};
-  WaveLds<MT>& L = lds.wave[wave];
-
-  for (int cb = kb0; cb < kb1; cb += CH) {
-    const int nb = min(CH, kb1 - cb);
-    // 1. every load of the chunk: activations first (needed first), then
-    //    the weights; lanes past the ends read zeros
-    float4 xv[MT][CH];
+  // byte offset of block cb + bi of this lane's row in tile r (kOob past the
+  // workgroup's rows or the chunk's nbb blocks)
+  auto w_off = [&](int r, int cb, int bi, int nbb) -> uint32_t {
+    const int row = r * kRows + nl;
+    return row < rows && bi < nbb ? static_cast<uint32_t>(row * K + cb + bi) * kBlockBytes : kOob;
+  };
+  using XT = typename XRaw<BF16>::type;
+  auto load_x = [&](int cb, int nbb, XT (&xv)[MT][CH]) {
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int bi = 0; bi < CH; ++bi) {
-        const uint32_t off = t < mt && bi < nb
+        const uint32_t off = t < mt && bi < nbb
                                  ? static_cast<uint32_t>(xrow[t] * a.ldx + (cb + bi) * kQK + 4 * lane)
                                  : kOob;
         xv[t][bi] = load_x4<BF16>(rx, off);
       }
-    BlockRegs rgb[CH], rub[GU ? CH : 1];
+  };
+
+  float yg[RT][4], yu[RT][4];
 #pragma unroll
-    for (int bi = 0; bi < CH; ++bi) {
-      const uint32_t off = nl < rows && bi < nb
-                               ? static_cast<uint32_t>(nl * K + cb + bi) * kBlockBytes
-                               : kOob;
-      load_block(rg, off, g, rgb[bi]);
-      if constexpr (GU) load_block(ru, off, g, rub[bi]);
-    }
-    // 2. activations -> operand layout in this wavefront's LDS
-    convert_chunk<MT>(L, xv, mt, nb, lane);
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) yg[r][i] = yu[r][i] = 0.f;
+  WaveLds<MT>& L = lds.wave[wave];
+
+  // Pipeline: the activations of chunk c+1 are loaded while chunk c is
+  // multiplied, and the weight registers of a block are refilled as soon as
+  // the block is consumed (with the same block of the next tile, or of tile
+  // 0 of the next chunk after the last tile), so loads stay in flight across
+  // tiles and chunks.
+  int cb = kb0;
+  int nb = min(CH, kb1 - cb);
+  XT xv[MT][CH];
+  load_x(cb, nb, xv);
+  BlockRegs rgb[CH], rub[GU ? CH : 1];
+#pragma unroll
+  for (int bi = 0; bi < CH; ++bi) {
+    const uint32_t off = w_off(0, cb, bi, nb);
+    load_block(rg, off, g, rgb[bi]);
+    if constexpr (GU) load_block(ru, off, g, rub[bi]);
+  }
+  // One chunk; HN: a next chunk exists (its activations and the weights of
+  // its first tile are loaded here).  The last chunk is peeled off so that no
+  // load sits under a branch whose result is used after it.
+  auto chunk = [&](auto hn) {
+    constexpr bool HN = decltype(hn)::value;
+    // 1. activations -> operand layout in this wavefront's LDS
+    convert_chunk<MT, XT>(L, xv, mt, nb, lane);
     lds_fence();
-    // 3. one MFMA chain per block and matrix; C element i of this lane is row
-    //    4g + i: token (4g + i) % HR, hi half when 4g + i < HR, lo when below R2
+    const int cn = cb + CH;
+    const int nbn = HN ? min(CH, kb1 - cn) : 0;
+    if constexpr (HN) load_x(cn, nbn, xv);
+    int shs[4];
 #pragma unroll
-    for (int bi = 0; bi < CH; ++bi) {
-      if (bi < nb) {  // uniform
-        float d, dmin;
-        v4f cm, cn;
-        int shs[4];
+    for (int i = 0; i < 4; ++i) shs[i] = L.shift[(4 * g + i) & (HR - 1)];
+    // 2. one MFMA chain per block, tile and matrix; C element i of this lane
+    //    is row 4g + i: token (4g + i) % HR, hi half when 4g + i < HR, lo when
+    //    below R2
 #pragma unroll
-        for (int i = 0; i < 4; ++i) shs[i] = L.shift[(4 * g + i) & (HR - 1)];
-        block_mfma<MT>(rgb[bi], g, L, bi, arow, d, dmin, cm, cn);
+    for (int r = 0; r < RT; ++r) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) yg[i] += ldexpf(fmaf(d, cm[i], -dmin * cn[i]), -shs[i]);
-        if constexpr (GU) {
-          block_mfma<MT>(rub[bi], g, L, bi, arow, d, dmin, cm, cn);
+      for (int bi = 0; bi < CH; ++bi) {
+        if (bi < nb) {  // uniform
+          float d, dmin;
+          v4f cmv, cnv;
+          block_mfma<MT>(rgb[bi], g, L, bi, arow, d, dmin, cmv, cnv);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) yu[i] += ldexpf(fmaf(d, cm[i], -dmin * cn[i]), -shs[i]);
+          for (int i = 0; i < 4; ++i) yg[r][i] += ldexpf(fmaf(d, cmv[i], -dmin * cnv[i]), -shs[i]);
+          if constexpr (GU) {
+            block_mfma<MT>(rub[bi], g, L, bi, arow, d, dmin, cmv, cnv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) yu[r][i] += ldexpf(fmaf(d, cmv[i], -dmin * cnv[i]), -shs[i]);
+          }
+        }
+        // refill the block's registers: next tile, or tile 0 of the next chunk
+        if (r + 1 < RT || HN) {  // compile-time
+          const uint32_t off = r + 1 < RT ? w_off(r + 1, cb, bi, nb) : w_off(0, cn, bi, nbn);
+          load_block(rg, off, g, rgb[bi]);
+          if constexpr (GU) load_block(ru, off, g, rub[bi]);
         }
       }
     }
     lds_fence();
-  }
+    cb = cn;
+    nb = nbn;
+  };
+  while (cb + CH < kb1) chunk(std::integral_constant<bool, true>{});  // uniform
+  if (cb < kb1) chunk(std::integral_constant<bool, false>{});         // uniform
 
-  __syncthreads();
+  // 3. add the W partial tiles of each row tile in a fixed order
   // C layout: lane holds rows 4g .. 4g+3 of weight row nl
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lds.red[0][wave][4 * g + i][nl] = yg[i];
-    if constexpr (GU) lds.red[GU ? 1 : 0][wave][4 * g + i][nl] = yu[i];
-  }
-  __syncthreads();
   const int t = tid / kRows;
-  const int r = tid % kRows;
-  if (t < mt && r < rows) {
-    float s = 0.f;
+  const int rr = tid % kRows;
 #pragma unroll
-    for (int w = 0; w < W; ++w) s += lds.red[0][w][t][r] + lds.red[0][w][HR + t][r];
-    float out = s;
-    if constexpr (GU) {
-      float su = 0.f;
+  for (int r = 0; r < RT; ++r) {
+    __syncthreads();
 #pragma unroll
-      for (int w = 0; w < W; ++w)
-        su += lds.red[GU ? 1 : 0][w][t][r] + lds.red[GU ? 1 : 0][w][HR + t][r];
-      out = silu_mul(s, su);
+    for (int i = 0; i < 4; ++i) {
+      lds.red[0][wave][4 * g + i][nl] = yg[r][i];
+      if constexpr (GU) lds.red[GU ? 1 : 0][wave][4 * g + i][nl] = yu[r][i];
     }
-    a.y[static_cast<size_t>(yrow[t]) * a.ldy + n0 + r] = out;
+    __syncthreads();
+    if (t < mt && r * kRows + rr < rows) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) s += lds.red[0][w][t][rr] + lds.red[0][w][HR + t][rr];
+      float out = s;
+      if constexpr (GU) {
+        float su = 0.f;
+#pragma unroll
+        for (int w = 0; w < W; ++w)
+          su += lds.red[GU ? 1 : 0][w][t][rr] + lds.red[GU ? 1 : 0][w][HR + t][rr];
+        out = silu_mul(s, su);
+      }
+      a.y[static_cast<size_t>(yrow[t]) * a.ldy + n0 + r * kRows + rr] = out;
+    }
   }
 }
 
-template <int MT, int W>
+template <int MT, int W, int RT>
 hipError_t dispatch_w(const GemvArgs& a, const dim3& grid, hipStream_t stream) {
   const bool gu = a.w_up != nullptr;
   const bool bf = a.x_bf16 != 0;
   if (gu) {
-    if (bf) gemv_mfma_kernel<MT, true, true, W><<<grid, dim3(64 * W), 0, stream>>>(a);
-    else gemv_mfma_kernel<MT, true, false, W><<<grid, dim3(64 * W), 0, stream>>>(a);
+    if (bf) gemv_mfma_kernel<MT, true, true, W, RT><<<grid, dim3(64 * W), 0, stream>>>(a);
+    else gemv_mfma_kernel<MT, true, false, W, RT><<<grid, dim3(64 * W), 0, stream>>>(a);
   } else {
-    if (bf) gemv_mfma_kernel<MT, false, true, W><<<grid, dim3(64 * W), 0, stream>>>(a);
-    else gemv_mfma_kernel<MT, false, false, W><<<grid, dim3(64 * W), 0, stream>>>(a);
+    if (bf) gemv_mfma_kernel<MT, false, true, W, RT><<<grid, dim3(64 * W), 0, stream>>>(a);
+    else gemv_mfma_kernel<MT, false, false, W, RT><<<grid, dim3(64 * W), 0, stream>>>(a);
   }
   return hipGetLastError();
 }
 
-// k is split over the wavefronts of a workgroup.  Eight wavefronts (two per
-// SIMD, so that one converts or multiplies while the other waits on memory)
-// need 128 KiB of LDS, one workgroup per CU: they pay off while all
-// workgroups fit on the 256 CUs at once, four wavefronts otherwise.
+// Tiles per workgroup: every workgroup converts its share of the activations
+// once per chunk and reuses them for RT tiles of 16 rows, RT chosen so that
+// about 256 workgroups cover all tiles (at most 3).  k is split over the
+// wavefronts of a workgroup: eight (two per SIMD, so that one converts or
+// multiplies while the other waits on memory; 128 KiB of LDS, one workgroup
+// per CU) while all workgroups fit on the 256 CUs at once, four otherwise.
+template <int MT, int RT>
+hipError_t dispatch_rt(const GemvArgs& a, int tiles, int slots, hipStream_t stream) {
+  const dim3 grid((tiles + RT - 1) / RT, slots);
+  if (static_cast<long long>(grid.x) * grid.y <= 256) return dispatch_w<MT, kWavesMax, RT>(a, grid, stream);
+  return dispatch_w<MT, 4, RT>(a, grid, stream);
+}
+
 template <int MT>
 hipError_t dispatch_m(const GemvArgs& a, hipStream_t stream) {
-  const dim3 grid((a.n + kRows - 1) / kRows, a.slot_expert ? a.slots : 1);
-  if (static_cast<long long>(grid.x) * grid.y <= 256) return dispatch_w<MT, kWavesMax>(a, grid, stream);
-  return dispatch_w<MT, 4>(a, grid, stream);
+  const int tiles = (a.n + kRows - 1) / kRows;
+  const int slots = a.slot_expert ? a.slots : 1;
+  const long long total = static_cast<long long>(tiles) * slots;
+  const long long rt = (total + 255) / 256;
+  if (rt <= 1) return dispatch_rt<MT, 1>(a, tiles, slots, stream);
+  if (rt == 2) return dispatch_rt<MT, 2>(a, tiles, slots, stream);
+  return dispatch_rt<MT, 3>(a, tiles, slots, stream);
 }
 
 }  // namespace
