@@ -78,13 +78,10 @@ int check_elems(int m, int k) {
 // Workspace layout of ffn_swiglu_q4k.
 struct FfnLayout {
   size_t total = 0;
-  // decode dense
-  size_t h = 0;
+  // decode dense (and MoE: h and the pair outputs of every (token, slot) pair)
+  size_t h = 0, y_pair = 0;
   // prefill
   size_t qx = 0, dx = 0, qh = 0, dh = 0;
-  // MoE
-  size_t slot_expert = 0, slot_count = 0, slot_x = 0, slot_y = 0, y_pair = 0;
-  int slots = 0;
 };
 
 int resolve_regime(int regime, int m) {
@@ -108,11 +105,6 @@ bool ffn_layout(int m, int hidden, int inter, int top_k, int regime, FfnLayout* 
   };
   if (top_k > 0) {
     const size_t pairs = M * static_cast<size_t>(top_k);
-    L->slots = static_cast<int>(pairs);
-    L->slot_expert = take(pairs * 4);
-    L->slot_count = take(pairs * 4);
-    L->slot_x = take(pairs * kMaxTokens * 4);
-    L->slot_y = take(pairs * kMaxTokens * 4);
     L->h = take(pairs * I * 4);
     L->y_pair = take(pairs * H * 4);
   } else if (regime == Q4K_REGIME_DECODE) {
@@ -282,11 +274,9 @@ int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int
   float* h = reinterpret_cast<float*>(ws + L.h);
 
   if (moe) {
-    SlotTable tab{reinterpret_cast<int32_t*>(ws + L.slot_expert), reinterpret_cast<int32_t*>(ws + L.slot_count),
-                  reinterpret_cast<int32_t*>(ws + L.slot_x), reinterpret_cast<int32_t*>(ws + L.slot_y)};
-    hipError_t e = launch_moe_route(ids, m, top_k, n_experts, tab, L.slots, s);
-    if (e != hipSuccess) return Q4K_ERR_LAUNCH;
-    const int cap = m < kMaxTokens ? m : kMaxTokens;
+    // Every (token, slot) pair is an independent pass over its expert's
+    // rows: gate/up on x row t (h row = pair), down on h row = pair (pair
+    // output row), then the slot-order weighted combine.
     GemvArgs gu{};
     gu.w = static_cast<const uint8_t*>(w_gate);
     gu.w_up = static_cast<const uint8_t*>(w_up);
@@ -298,13 +288,14 @@ int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int
     gu.ldy = inter;
     gu.n = inter;
     gu.k = hidden;
-    gu.m = cap;
-    gu.slot_expert = tab.expert;
-    gu.slot_count = tab.count;
-    gu.slot_x = tab.xrow;
-    gu.slot_y = tab.yrow;
-    gu.slots = L.slots;
-    if ((e = launch_gemv(gu, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
+    gu.m = m;
+    gu.ids = ids;
+    gu.x_by_token = 1;
+    gu.top_k = top_k;
+    gu.n_experts = n_experts;
+    gu.pairs = m * top_k;
+    hipError_t e = launch_gemv(gu, s);
+    if (e != hipSuccess) return Q4K_ERR_LAUNCH;
     float* y_pair = reinterpret_cast<float*>(ws + L.y_pair);
     GemvArgs dn = gu;
     dn.w = static_cast<const uint8_t*>(w_down);
@@ -317,7 +308,7 @@ int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int
     dn.ldy = hidden;
     dn.n = hidden;
     dn.k = inter;
-    dn.slot_x = tab.yrow;  // the down pass reads the pair's own h row
+    dn.x_by_token = 0;
     if ((e = launch_gemv(dn, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
     return launch_status(launch_moe_combine(y_pair, wts, ids, m, top_k, n_experts, hidden, y, s));
   }

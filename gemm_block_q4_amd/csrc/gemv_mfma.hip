@@ -276,26 +276,7 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(GemvArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = a.k / kQK;
 
-  int expert = 0, mt = a.m;
-  int xrow[MT], yrow[MT];
-  if (a.slot_expert != nullptr) {
-    const int slot = blockIdx.y;
-    expert = a.slot_expert[slot];
-    if (expert < 0) return;  // uniform over the workgroup, before any barrier
-    mt = min(a.slot_count[slot], MT);
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      xrow[t] = t < mt ? a.slot_x[slot * kMaxTokens + t] : 0;
-      yrow[t] = t < mt ? a.slot_y[slot * kMaxTokens + t] : 0;
-    }
-  } else {
-    mt = min(mt, MT);
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      xrow[t] = t < mt ? t : 0;
-      yrow[t] = t;
-    }
-  }
+  const int mt = min(a.m, MT);  // live tokens (rows of x and y)
 
   // this workgroup's RT tiles of 16 rows
   const int n0 = blockIdx.x * (RT * kRows);
@@ -304,8 +285,7 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(GemvArgs a) {
   const int g = lane >> 4;    // lane group: K slots 8g .. 8g+7
   const int arow = nl & (R2 - 1);
   // the workgroup's rows of each matrix (at most 48 rows * 128 blocks * 144 bytes)
-  const size_t wofs = static_cast<size_t>(expert) * a.mat_bytes +
-                      static_cast<size_t>(n0) * K * kBlockBytes;
+  const size_t wofs = static_cast<size_t>(n0) * K * kBlockBytes;
   const uint32_t wbytes = static_cast<uint32_t>(rows) * static_cast<uint32_t>(K) * kBlockBytes;
   const rsrc_t rg = make_rsrc(a.w + wofs, wbytes);
   const rsrc_t ru = GU ? make_rsrc(a.w_up + wofs, wbytes) : rg;
@@ -329,7 +309,7 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(GemvArgs a) {
 #pragma unroll
       for (int bi = 0; bi < CH; ++bi) {
         const uint32_t off = t < mt && bi < nbb
-                                 ? static_cast<uint32_t>(xrow[t] * a.ldx + (cb + bi) * kQK + 4 * lane)
+                                 ? static_cast<uint32_t>(t * a.ldx + (cb + bi) * kQK + 4 * lane)
                                  : kOob;
         xv[t][bi] = load_x4<BF16>(rx, off);
       }
@@ -431,7 +411,7 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(GemvArgs a) {
           su += lds.red[GU ? 1 : 0][w][t][rr] + lds.red[GU ? 1 : 0][w][HR + t][rr];
         out = silu_mul(s, su);
       }
-      a.y[static_cast<size_t>(yrow[t]) * a.ldy + n0 + r * kRows + rr] = out;
+      a.y[static_cast<size_t>(t) * a.ldy + n0 + r * kRows + rr] = out;
     }
   }
 }
@@ -457,8 +437,8 @@ hipError_t dispatch_w(const GemvArgs& a, const dim3& grid, hipStream_t stream) {
 // multiplies while the other waits on memory; 128 KiB of LDS, one workgroup
 // per CU) while all workgroups fit on the 256 CUs at once, four otherwise.
 template <int MT, int RT>
-hipError_t dispatch_rt(const GemvArgs& a, int tiles, int slots, hipStream_t stream) {
-  const dim3 grid((tiles + RT - 1) / RT, slots);
+hipError_t dispatch_rt(const GemvArgs& a, int tiles, hipStream_t stream) {
+  const dim3 grid((tiles + RT - 1) / RT);
   if (static_cast<long long>(grid.x) * grid.y <= 256) return dispatch_w<MT, kWavesMax, RT>(a, grid, stream);
   return dispatch_w<MT, 4, RT>(a, grid, stream);
 }
@@ -466,12 +446,10 @@ hipError_t dispatch_rt(const GemvArgs& a, int tiles, int slots, hipStream_t stre
 template <int MT>
 hipError_t dispatch_m(const GemvArgs& a, hipStream_t stream) {
   const int tiles = (a.n + kRows - 1) / kRows;
-  const int slots = a.slot_expert ? a.slots : 1;
-  const long long total = static_cast<long long>(tiles) * slots;
-  const long long rt = (total + 255) / 256;
-  if (rt <= 1) return dispatch_rt<MT, 1>(a, tiles, slots, stream);
-  if (rt == 2) return dispatch_rt<MT, 2>(a, tiles, slots, stream);
-  return dispatch_rt<MT, 3>(a, tiles, slots, stream);
+  const int rt = (tiles + 255) / 256;
+  if (rt <= 1) return dispatch_rt<MT, 1>(a, tiles, stream);
+  if (rt == 2) return dispatch_rt<MT, 2>(a, tiles, stream);
+  return dispatch_rt<MT, 3>(a, tiles, stream);
 }
 
 }  // namespace

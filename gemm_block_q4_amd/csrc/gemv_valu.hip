@@ -280,7 +280,15 @@ __device__ __forceinline__ void convert_unit(const float4 (&xr)[4], int u, bool 
   }
 }
 
-template <bool GU, bool BF16, bool MOE, int LAYOUT, int XU, int PF>
+// Kernel modes: one dense matrix (grid.y = 1), or the MoE pass (grid.y =
+// (token, slot) pair p: the rows of expert ids[p] on x row p / top_k (gate /
+// up) or p (down), output row p; a pair with an id outside [0, n_experts)
+// does nothing).  Every pair is independent, so an expert chosen by several
+// tokens streams its rows once per pair (from L2 when the pairs' workgroups
+// run close together), and no workgroup runs passes back to back.
+enum Mode { kDense = 0, kPair = 1 };
+
+template <bool GU, bool BF16, int MODE, int LAYOUT, int XU, int PF>
 __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo geo) {
   constexpr bool WIDE = LAYOUT == kWide;
   constexpr bool SEG64 = LAYOUT != kNarrow;
@@ -297,16 +305,6 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
   // ahead of the first weight load)
   asm volatile("" ::"s"(a.w), "s"(a.w_up), "s"(a.x), "s"(a.k), "s"(a.n), "s"(geo.rows), "s"(geo.step),
                "s"(geo.lpr_log), "s"(geo.wslot), "s"(geo.wpart));
-
-  int expert = 0, xrow = 0, yrow = 0;
-  if constexpr (MOE) {
-    const int slot = blockIdx.y;
-    expert = a.slot_expert[slot];
-    // uniform over the workgroup, before any barrier
-    if (expert < 0 || a.slot_count[slot] < 1) return;
-    xrow = a.slot_x[slot * kMaxTokens];
-    yrow = a.slot_y[slot * kMaxTokens];
-  }
 
   // this lane's row slot (within a step) and slice position
   int rslot, slice;
@@ -328,161 +326,182 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
   // while it*step < rows
   const int row0 = blockIdx.x * geo.rows;
   const int rows = min(geo.rows, a.n - row0);
-
-  // buffer resources: this workgroup's rows of the matrices (under 2^31 bytes
-  // by construction of the geometry) and the token's activation row
-  const size_t wofs = static_cast<size_t>(expert) * a.mat_bytes +
-                      static_cast<size_t>(row0) * K * kBlockBytes;
   const uint32_t wbytes = static_cast<uint32_t>(rows) * static_cast<uint32_t>(K) * kBlockBytes;
-  const rsrc_t rg = make_rsrc(a.w + wofs, wbytes);
-  const rsrc_t ru = GU ? make_rsrc(a.w_up + wofs, wbytes) : rg;
-  const size_t xel = static_cast<size_t>(xrow) * a.ldx;
-  const rsrc_t rx = BF16 ? make_rsrc(static_cast<const uint16_t*>(a.x) + xel, 2u * a.k)
-                         : make_rsrc(static_cast<const float*>(a.x) + xel, 4u * a.k);
+  // Products of uniform values pass through an opaque scalar move: the
+  // compiler would otherwise fold them with a lane value into a 64-bit
+  // multiply-add whose (unused) high addend register may be a load still in
+  // flight, and wait for it (it sees through readfirstlane of a scalar).
+  auto uni = [](int v) -> int {
+    int r;
+    asm("s_mov_b32 %0, %1" : "=s"(r) : "s"(v));
+    return r;
+  };
   // byte offset of this lane's block in step it: base + it * stride (adds
   // only), kOob past the last row
   const uint32_t stride = static_cast<uint32_t>(geo.step * K) * kBlockBytes;
   const uint32_t base = static_cast<uint32_t>(rslot * K + b) * kBlockBytes;
-  // Products of uniform values go through readfirstlane: the compiler would
-  // otherwise fold them with a lane value into a 64-bit multiply-add whose
-  // (unused) high addend register may be a load still in flight, and wait
-  // for it.
-  auto uni = [](int v) -> int { return __builtin_amdgcn_readfirstlane(v); };
   auto step_off = [&](int it, uint32_t off) -> uint32_t {
     return lane_ok && rslot < rows - uni(it * geo.step) ? off : kOob;
   };
+  // Unit j of this thread's activation units (XU of them, XU * nthr >= units
+  // by construction of the launch).
   auto unit_off = [&](int u, int c) -> uint32_t {
     return u < units ? static_cast<uint32_t>(16 * u + 4 * c) : kOob;
   };
-
-  // 1. this thread's activation units (XU of them, XU * nthr >= units by
-  //    construction of the launch), loaded before any weight
-  float4 xr[XU][4];
-#pragma unroll
-  for (int j = 0; j < XU; ++j)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) xr[j][c] = load_x4<BF16>(rx, unit_off(tid + j * nthr, c));
-
-  // 2. weight loads of the first PF steps
-  RawSlice sg[PF], su[GU ? PF : 1];
-#pragma unroll
-  for (int p = 0; p < PF; ++p) {
-    const uint32_t off = step_off(p, base + static_cast<uint32_t>(uni(p * static_cast<int>(stride))));
-    load_slice(rg, off, g, sg[p]);
-    if constexpr (GU) load_slice(ru, off, g, su[p]);
-  }
-
-  // 3. activations -> digits in LDS, once per workgroup (the loop bounds are
-  //    uniform, so every quad converts together)
   uint32_t* dig = smem_u;                                                         // [S][48]
   float* xinfo = reinterpret_cast<float*>(smem_u + static_cast<size_t>(S) * 48);  // [S][4]
-#pragma unroll
-  for (int j = 0; j < XU; ++j) {
-    const int u = tid + j * nthr;
-    convert_unit(xr[j], u, u < units, dig, xinfo);
-  }
-  // A barrier without a memory fence: the digits are LDS writes, complete at
-  // lgkmcnt(0), and a fence would also wait for the weight loads in flight.
-  __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  XSlice xs;
-  {
-    const uint32_t* base = dig + static_cast<size_t>(lane_ok ? slice : 0) * 48;
-#pragma unroll
-    for (int d = 0; d < 3; ++d)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 t4 = *reinterpret_cast<const uint4*>(base + 16 * d + 4 * i);
-        xs.dg[d][4 * i] = t4.x; xs.dg[d][4 * i + 1] = t4.y;
-        xs.dg[d][4 * i + 2] = t4.z; xs.dg[d][4 * i + 3] = t4.w;
-      }
-    const float4 inf = *reinterpret_cast<const float4*>(xinfo + 4 * (lane_ok ? slice : 0));
-    xs.scale = inf.x; xs.sum0 = inf.y; xs.sum1 = inf.z;
-  }
-
-  // 4. row loop: consume step p while steps p+1 .. p+PF-1 are in flight.  The
-  //    loads are never under a branch (rows past the end read kOob), the last
-  //    group issues none, and inactive lanes contribute 0 to the DPP sums.
-  float* part = reinterpret_cast<float*>(smem_u + x_words(S));  // [GU?2:1][rows][wr]
+  float* part = reinterpret_cast<float*>(smem_u + x_words(S));                   // [GU?2:1][rows][wr]
   const int seg_mask = SEG64 ? 63 : (1 << geo.lpr_log) - 1;
-  auto dot = [&](const RawSlice& raw, bool ok) -> float {
-    const float v = slice_dot(expand(raw), fsel, xs);
-    return ok ? v : 0.f;
-  };
-  auto finish = [&](float (&o)[PF], float (&ou)[PF], int it0) {
+
+  // One pass over the workgroup's rows of one matrix for one activation row;
+  // writes y row `yrow`.
+  auto pass = [&](size_t mofs, int xrow, int yrow) {
+    const size_t wofs = mofs + static_cast<size_t>(row0) * K * kBlockBytes;
+    const rsrc_t rg = make_rsrc(a.w + wofs, wbytes);
+    const rsrc_t ru = GU ? make_rsrc(a.w_up + wofs, wbytes) : rg;
+    const size_t xel = static_cast<size_t>(xrow) * a.ldx;
+    const rsrc_t rx = BF16 ? make_rsrc(static_cast<const uint16_t*>(a.x) + xel, 2u * a.k)
+                           : make_rsrc(static_cast<const float*>(a.x) + xel, 4u * a.k);
+
+    // 1. this thread's activation units, loaded before any weight
+    float4 xr[XU][4];
+#pragma unroll
+    for (int j = 0; j < XU; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xr[j][c] = load_x4<BF16>(rx, unit_off(tid + j * nthr, c));
+
+    // 2. weight loads of the first PF steps
+    RawSlice sg[PF], su[GU ? PF : 1];
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      o[p] = SEG64 ? segment_sum<64>(o[p]) : segment_sum_rt(o[p], seg_mask + 1);
-      if constexpr (GU) ou[p] = SEG64 ? segment_sum<64>(ou[p]) : segment_sum_rt(ou[p], seg_mask + 1);
-    }
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int r = uni((it0 + p) * geo.step) + rslot;
-      // the segment's last lane holds the row sum (it may be a padding lane)
-      if (rslot < geo.step && r < rows && (lane & seg_mask) == seg_mask) {
-        if constexpr (!WIDE) {
-          float out = o[p];
-          if constexpr (GU) out = silu_mul(o[p], ou[p]);
-          a.y[static_cast<size_t>(yrow) * a.ldy + row0 + r] = out;
-        } else {
-          part[r * geo.wr + (slice >> 6)] = o[p];
-          if constexpr (GU) part[(rows + r) * geo.wr + (slice >> 6)] = ou[p];
-        }
-      }
-    }
-  };
-  int it0 = 0;
-  uint32_t next = base + PF * stride;  // offset of step it0 + PF
-  for (; (it0 + PF) * geo.step < rows; it0 += PF, next += PF * stride) {  // uniform; a later group exists
-    float o[PF], ou[PF];
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const bool ok = lane_ok && rslot < rows - uni((it0 + p) * geo.step);
-      o[p] = dot(sg[p], ok);
-      ou[p] = 0.f;
-      if constexpr (GU) ou[p] = dot(su[p], ok);
-      const uint32_t off = step_off(it0 + p + PF, next + static_cast<uint32_t>(uni(p * static_cast<int>(stride))));
+      const uint32_t off = step_off(p, base + static_cast<uint32_t>(uni(p * static_cast<int>(stride))));
       load_slice(rg, off, g, sg[p]);
       if constexpr (GU) load_slice(ru, off, g, su[p]);
     }
-    finish(o, ou, it0);
-  }
-  {  // the last group: nothing left to load
-    float o[PF], ou[PF];
+
+    // 3. activations -> digits in LDS, once per workgroup (the loop bounds are
+    //    uniform, so every quad converts together)
 #pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      o[p] = 0.f;
-      ou[p] = 0.f;
-      if ((it0 + p) * geo.step < rows) {  // uniform
+    for (int j = 0; j < XU; ++j) {
+      const int u = tid + j * nthr;
+      convert_unit(xr[j], u, u < units, dig, xinfo);
+    }
+    // A barrier without a memory fence: the digits are LDS writes, complete
+    // at lgkmcnt(0), and a fence would also wait for the weight loads in
+    // flight.
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    XSlice xs;
+    {
+      const uint32_t* dbase = dig + static_cast<size_t>(lane_ok ? slice : 0) * 48;
+#pragma unroll
+      for (int d = 0; d < 3; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 t4 = *reinterpret_cast<const uint4*>(dbase + 16 * d + 4 * i);
+          xs.dg[d][4 * i] = t4.x; xs.dg[d][4 * i + 1] = t4.y;
+          xs.dg[d][4 * i + 2] = t4.z; xs.dg[d][4 * i + 3] = t4.w;
+        }
+      const float4 inf = *reinterpret_cast<const float4*>(xinfo + 4 * (lane_ok ? slice : 0));
+      xs.scale = inf.x; xs.sum0 = inf.y; xs.sum1 = inf.z;
+    }
+
+    // 4. row loop: consume step p while steps p+1 .. p+PF-1 are in flight.
+    //    The loads are never under a branch (rows past the end read kOob),
+    //    the last group issues none, and inactive lanes contribute 0 to the
+    //    DPP sums.
+    auto dot = [&](const RawSlice& raw, bool ok) -> float {
+      const float v = slice_dot(expand(raw), fsel, xs);
+      return ok ? v : 0.f;
+    };
+    auto finish = [&](float (&o)[PF], float (&ou)[PF], int it0) {
+#pragma unroll
+      for (int p = 0; p < PF; ++p) {
+        o[p] = SEG64 ? segment_sum<64>(o[p]) : segment_sum_rt(o[p], seg_mask + 1);
+        if constexpr (GU) ou[p] = SEG64 ? segment_sum<64>(ou[p]) : segment_sum_rt(ou[p], seg_mask + 1);
+      }
+#pragma unroll
+      for (int p = 0; p < PF; ++p) {
+        const int r = uni((it0 + p) * geo.step) + rslot;
+        // the segment's last lane holds the row sum (it may be a padding lane)
+        if (rslot < geo.step && r < rows && (lane & seg_mask) == seg_mask) {
+          if constexpr (!WIDE) {
+            float out = o[p];
+            if constexpr (GU) out = silu_mul(o[p], ou[p]);
+            a.y[static_cast<size_t>(yrow) * a.ldy + row0 + r] = out;
+          } else {
+            part[r * geo.wr + (slice >> 6)] = o[p];
+            if constexpr (GU) part[(rows + r) * geo.wr + (slice >> 6)] = ou[p];
+          }
+        }
+      }
+    };
+    int it0 = 0;
+    uint32_t next = base + PF * stride;  // offset of step it0 + PF
+    for (; (it0 + PF) * geo.step < rows; it0 += PF, next += PF * stride) {  // uniform; a later group exists
+      float o[PF], ou[PF];
+#pragma unroll
+      for (int p = 0; p < PF; ++p) {
         const bool ok = lane_ok && rslot < rows - uni((it0 + p) * geo.step);
         o[p] = dot(sg[p], ok);
+        ou[p] = 0.f;
         if constexpr (GU) ou[p] = dot(su[p], ok);
+        const uint32_t off = step_off(it0 + p + PF, next + static_cast<uint32_t>(uni(p * static_cast<int>(stride))));
+        load_slice(rg, off, g, sg[p]);
+        if constexpr (GU) load_slice(ru, off, g, su[p]);
+      }
+      finish(o, ou, it0);
+    }
+    {  // the last group: nothing left to load
+      float o[PF], ou[PF];
+#pragma unroll
+      for (int p = 0; p < PF; ++p) {
+        o[p] = 0.f;
+        ou[p] = 0.f;
+        if ((it0 + p) * geo.step < rows) {  // uniform
+          const bool ok = lane_ok && rslot < rows - uni((it0 + p) * geo.step);
+          o[p] = dot(sg[p], ok);
+          if constexpr (GU) ou[p] = dot(su[p], ok);
+        }
+      }
+      finish(o, ou, it0);
+    }
+    if constexpr (WIDE) {
+      __syncthreads();
+      // 5. rows that span wavefronts: add the per-wavefront sums in order
+      for (int r = tid; r < rows; r += nthr) {
+        float s = 0.f, su_ = 0.f;
+        for (int w = 0; w < geo.wr; ++w) {
+          s += part[r * geo.wr + w];
+          if constexpr (GU) su_ += part[(rows + r) * geo.wr + w];
+        }
+        float out = s;
+        if constexpr (GU) out = silu_mul(s, su_);
+        a.y[static_cast<size_t>(yrow) * a.ldy + row0 + r] = out;
       }
     }
-    finish(o, ou, it0);
-  }
-  if constexpr (!WIDE) return;
-  __syncthreads();
-  // 5. rows that span wavefronts: add the per-wavefront sums in order
-  for (int r = tid; r < rows; r += nthr) {
-    float s = 0.f, su_ = 0.f;
-    for (int w = 0; w < geo.wr; ++w) {
-      s += part[r * geo.wr + w];
-      if constexpr (GU) su_ += part[(rows + r) * geo.wr + w];
-    }
-    float out = s;
-    if constexpr (GU) out = silu_mul(s, su_);
-    a.y[static_cast<size_t>(yrow) * a.ldy + row0 + r] = out;
+  };
+
+  if constexpr (MODE == kDense) {
+    pass(0, 0, 0);
+  } else {
+    const int pr = blockIdx.y;
+    const int e = a.ids[pr];
+    if (e < 0 || e >= a.n_experts) return;  // uniform, before any barrier
+    pass(static_cast<size_t>(e) * a.mat_bytes, a.x_by_token ? pr / a.top_k : pr, pr);
   }
 }
 
+// LDS bytes: digits and slice info, and the row partials when a row spans
+// wavefronts.
 size_t lds_bytes(const Geo& geo, int k, bool gu) {
   size_t words = x_words(4 * (k / kQK));
   if (geo.wr > 1) words += static_cast<size_t>(gu ? 2 : 1) * geo.rows * geo.wr;
   return words * sizeof(uint32_t);
 }
 
-Geo make_geo(int n, int k, int slots, bool gu) {
+Geo make_geo(int n, int k, int slots, bool gu, int mode) {
+  const int pf = gu ? 2 : 4;  // steps in flight per wavefront
   Geo g{};
   const int K = k / kQK;
   const int l = 4 * K;
@@ -514,21 +533,26 @@ Geo make_geo(int n, int k, int slots, bool gu) {
   if (want > n) want = n;
   if (want < g.step) want = g.step;
   g.rows = static_cast<int>((want + g.step - 1) / g.step * g.step);
+  // MoE pairs: one prefetch group per workgroup (no serial memory round
+  // trips; the many pairs fill the chip)
+  if (mode == kPair && g.rows > pf * g.step) g.rows = pf * g.step;
   const int cap_bytes = static_cast<int>((static_cast<size_t>(kOob) - 1) / (static_cast<size_t>(K) * kBlockBytes)) /
                         g.step * g.step;
   if (g.rows > cap_bytes) g.rows = cap_bytes;
-  if (g.wr > 1) {
+  // (per row: the partials of a row that spans wavefronts)
+  const size_t per_row = g.wr > 1 ? static_cast<size_t>(gu ? 2 : 1) * g.wr : 0;
+  if (per_row > 0) {
     const size_t free_words = kLdsMax / sizeof(uint32_t) - x_words(l);
-    const int cap = static_cast<int>(free_words / (static_cast<size_t>(gu ? 2 : 1) * g.wr)) / g.step * g.step;
+    const int cap = static_cast<int>(free_words / per_row) / g.step * g.step;
     if (g.rows > cap) g.rows = cap;
   }
   return g;
 }
 
-template <bool GU, bool BF16, bool MOE, int LAYOUT, int XU>
-hipError_t launch_layout(const GemvArgs& a, const Geo& geo, size_t lds, hipStream_t stream) {
+template <bool GU, bool BF16, int MODE, int LAYOUT, int XU>
+hipError_t launch_layout(const GemvArgs& a, const Geo& geo, size_t lds, int grid_y, hipStream_t stream) {
   constexpr int PF = GU ? 2 : 4;
-  auto kern = gemv_d4_kernel<GU, BF16, MOE, LAYOUT, XU, PF>;
+  auto kern = gemv_d4_kernel<GU, BF16, MODE, LAYOUT, XU, PF>;
   static bool big_lds = false;  // the opt-in is per kernel and stays set
   if (lds > 64 * 1024 && !big_lds) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -537,16 +561,16 @@ hipError_t launch_layout(const GemvArgs& a, const Geo& geo, size_t lds, hipStrea
     if (e != hipSuccess) return e;
     big_lds = true;
   }
-  const int slots = MOE ? a.slots : 1;
-  const dim3 grid((a.n + geo.rows - 1) / geo.rows, slots);
+  const dim3 grid((a.n + geo.rows - 1) / geo.rows, grid_y);
   kern<<<grid, dim3(geo.waves * 64), lds, stream>>>(a, geo);
   return hipGetLastError();
 }
 
-template <bool GU, bool BF16, bool MOE>
-hipError_t launch_moe(const GemvArgs& a, hipStream_t stream) {
-  const int slots = MOE ? a.slots : 1;
-  const Geo geo = make_geo(a.n, a.k, slots, GU);
+template <bool GU, bool BF16, int MODE>
+hipError_t launch_mode(const GemvArgs& a, hipStream_t stream) {
+  // grid rows: the MoE pairs, or the single dense matrix
+  const int grid_y = MODE == kPair ? a.pairs : 1;
+  const Geo geo = make_geo(a.n, a.k, grid_y, GU, MODE);
   const size_t lds = lds_bytes(geo, a.k, GU);
   if (geo.rows < geo.step || lds > kLdsMax) return hipErrorInvalidValue;
   // activation units (16 values) per thread: one when a row fits a wavefront
@@ -555,24 +579,26 @@ hipError_t launch_moe(const GemvArgs& a, hipStream_t stream) {
   const int units = 16 * (a.k / kQK);
   const int nthr = geo.waves * 64;
   if (geo.wr > 1) {
-    if (units <= 2 * nthr) return launch_layout<GU, BF16, MOE, kWide, 2>(a, geo, lds, stream);
-    if (units <= 4 * nthr) return launch_layout<GU, BF16, MOE, kWide, 4>(a, geo, lds, stream);
+    if (units <= 2 * nthr) return launch_layout<GU, BF16, MODE, kWide, 2>(a, geo, lds, grid_y, stream);
+    if (units <= 4 * nthr) return launch_layout<GU, BF16, MODE, kWide, 4>(a, geo, lds, grid_y, stream);
     return hipErrorInvalidValue;
   }
   if (units > nthr) return hipErrorInvalidValue;
-  if (geo.lpr == 64) return launch_layout<GU, BF16, MOE, kOneWave, 1>(a, geo, lds, stream);
-  return launch_layout<GU, BF16, MOE, kNarrow, 1>(a, geo, lds, stream);
+  if (geo.lpr == 64) return launch_layout<GU, BF16, MODE, kOneWave, 1>(a, geo, lds, grid_y, stream);
+  return launch_layout<GU, BF16, MODE, kNarrow, 1>(a, geo, lds, grid_y, stream);
 }
 
 template <bool GU, bool BF16>
 hipError_t launch_d4(const GemvArgs& a, hipStream_t stream) {
-  return a.slot_expert ? launch_moe<GU, BF16, true>(a, stream) : launch_moe<GU, BF16, false>(a, stream);
+  if (a.ids != nullptr) return launch_mode<GU, BF16, kPair>(a, stream);
+  return launch_mode<GU, BF16, kDense>(a, stream);
 }
 
 }  // namespace
 
-// One token and k up to 32768: at most 8 wavefronts per row, and the digits of
-// all activations (208 bytes per 64 values, 104 KiB at k = 32768) fit in LDS.
+// One token (or the MoE passes, one routed pair at a time) and k up to 32768:
+// at most 8 wavefronts per row, and the digits of all activations (208 bytes
+// per 64 values, 104 KiB at k = 32768) fit in LDS.
 bool gemv_valu_fits(int m, int k) { return m == 1 && k <= 32768; }
 
 hipError_t launch_gemv_valu(const GemvArgs& a, hipStream_t stream) {
@@ -583,7 +609,7 @@ hipError_t launch_gemv_valu(const GemvArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream) {
-  if (gemv_valu_fits(a.m, a.k)) return launch_gemv_valu(a, stream);
+  if (a.ids != nullptr || gemv_valu_fits(a.m, a.k)) return launch_gemv_valu(a, stream);
   return launch_gemv_mfma(a, stream);
 }
 

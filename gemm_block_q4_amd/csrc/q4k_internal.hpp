@@ -9,16 +9,8 @@
 
 namespace q4k {
 
-// Routing table of the MoE decode path (device memory, written by the route
-// kernel).  Slot i holds up to kMaxTokens (pair) entries of one expert.
-struct SlotTable {
-  int32_t* expert;  // [slots]  expert id, -1 = unused slot
-  int32_t* count;   // [slots]  entries in the slot
-  int32_t* xrow;    // [slots][8] input row of each entry
-  int32_t* yrow;    // [slots][8] output row of each entry
-};
-
-// GEMV over one or many (expert, token set) slots.
+// GEMV over one dense matrix, or one of the two MoE passes over expert banks
+// (expert e's matrix at e * mat_bytes).
 struct GemvArgs {
   const uint8_t* w;      // weight bank (expert 0 at offset 0)
   const uint8_t* w_up;   // up bank for the fused gate/up pass, else nullptr
@@ -30,12 +22,16 @@ struct GemvArgs {
   int ldy;
   int n;                 // output rows per matrix
   int k;                 // input columns (multiple of 256)
-  int m;                 // dense mode: tokens (rows of x / y)
-  const int32_t* slot_expert;  // nullptr: dense mode (single slot, expert 0)
-  const int32_t* slot_count;
-  const int32_t* slot_x;
-  const int32_t* slot_y;
-  int slots;
+  int m;                 // tokens (rows of x / y in the dense mode)
+  // MoE (ids == nullptr: one dense matrix).  Pair p = t * top_k + s routes
+  // token t to expert ids[p]; grid row p runs the rows of that expert on x
+  // row p / top_k (x_by_token) or p and writes y row p.  Ids outside
+  // [0, n_experts) are skipped.
+  const int32_t* ids;
+  int x_by_token;
+  int top_k;
+  int n_experts;
+  int pairs;
 };
 
 // Dispatches to the VALU kernel (few tokens) or the matrix-core kernel.
@@ -58,11 +54,11 @@ struct MmqArgs {
 
 hipError_t launch_mmq(const MmqArgs& a, hipStream_t stream);
 
-hipError_t launch_moe_route(const int32_t* ids, int m, int top_k, int n_experts,
-                            const SlotTable& t, int slots, hipStream_t stream);
+// y[t] = sum_{s < top_k} wts[t][s] * y_pair[t * top_k + s] in slot order
+// (pairs with an id outside [0, n_experts) skipped).
+hipError_t launch_moe_combine(const float* y_pair, const float* wts, const int32_t* ids, int m,
+                              int top_k, int n_experts, int hidden, float* y, hipStream_t stream);
 
-hipError_t launch_moe_combine(const float* y_pair, const float* wts, const int32_t* ids,
-                              int m, int top_k, int n_experts, int hidden, float* y,
-                              hipStream_t stream);
+
 
 }  // namespace q4k
