@@ -21,12 +21,22 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   const int t = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (t >= m || c >= hidden) return;
+  // eight slots per round: all their loads are issued (on clamped, valid
+  // indices) before the first is used; the sum stays in slot order
   float acc = 0.f;
-  for (int s = 0; s < top_k; ++s) {
-    const int p = t * top_k + s;
-    const int e = ids[p];
-    const float v = y_pair[static_cast<size_t>(p) * hidden + c];
-    acc = e >= 0 && e < n_experts ? fmaf(wts[p], v, acc) : acc;
+  for (int s0 = 0; s0 < top_k; s0 += 8) {
+    int e[8];
+    float w[8], v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = t * top_k + min(s0 + i, top_k - 1);
+      const int id = ids[p];
+      e[i] = s0 + i < top_k ? id : -1;
+      w[i] = wts[p];
+      v[i] = y_pair[static_cast<size_t>(p) * hidden + c];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = e[i] >= 0 && e[i] < n_experts ? fmaf(w[i], v[i], acc) : acc;
   }
   y[static_cast<size_t>(t) * hidden + c] = acc;
 }
