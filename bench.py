@@ -36,10 +36,10 @@ ROTATE_BYTES = 1 << 30         # per rotated tensor set
 # WRITE_SIZE (each scaled by what it reads for a copy of known size; summary and commands in
 # profiles/gemv_d4_decode_sweep_hbm_traffic.md) for the kernel sources with these SHA-256
 # digests.  Reported only while the sources still match.
-TRAFFIC_SWEEP_BYTES = 61267597
+TRAFFIC_SWEEP_BYTES = 61266575
 TRAFFIC_SOURCES = {
     "gemm_block_q4_amd/csrc/gemv_valu.hip":
-        "bfaff7adac514b16bd5ceb2c8b89c5f1035d8657257f504812cbd096ac1cf71e",
+        "c3c6d1ca62c440a934ea02c250400c8146e4c8959c0b3056c3fad48c35f4cb1f",
     "gemm_block_q4_amd/csrc/q4k_device.hpp":
         "0ca9cfd803b914df0ad564490c5fd4e9deb5aaf1f4e89c866e6dd71f630d251d",
 }
@@ -309,7 +309,7 @@ def main():
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(),
                     traffic_scope="HBM bytes of the three sweep launches (same scope as achieved)",
-                    kernel="gemv_d4_kernel<false, false, false, 1|2, 1|2, 4> (q4k_gemv, m=1; layout 1 for k=4096, 2 for k=11008)",
+                    kernel="gemv_d4_kernel<false, false, 0, 1|2, 1|2, 4> (q4k_gemv, m=1; layout 1 for k=4096, 2 for k=11008)",
                     per_shape=[dict(n=p["n"], k=p["k"], us=round(p["us"], 3), gbs=round(p["gbs"], 1))
                                for p in per_shape])
 
