@@ -57,6 +57,17 @@ def test_prefill_ffn_small(lib, m, regime):
     assert orc.relative_l2(y, ref) <= TOL
 
 
+@pytest.mark.parametrize("m,hidden,inter", [(1, 512, 768), (3, 512, 768), (6, 4608, 512)])
+def test_decode_ffn_bf16_input(lib, m, hidden, inter):
+    # bf16 activations through the one-token and the matrix-core GEMVs
+    say(f"ffn decode bf16 x m={m} {hidden}/{inter}")
+    wg, wu, wd = synth.dense_ffn_weights(93, hidden, inter)
+    x = synth.activations(93, m, hidden, outliers=True, sub=m)
+    y = ffn_gpu(lib, wg, wu, wd, x, hidden, inter, regime=1, bf16=True)
+    xb = synth.bf16_bits_to_f32(synth.to_bf16_bits(x))
+    assert orc.relative_l2(y, orc.ffn_decode(wg, wu, wd, hidden, inter, xb)) <= TOL
+
+
 def test_decode_regime_forced_m8_matches(lib):
     say("ffn decode regime forced, m=8, 512/768")
     hidden, inter = 512, 768
@@ -83,13 +94,15 @@ def test_prefill_ffn_full_size(lib, prefill_weights, m, tokens):
     assert np.all(np.isfinite(y))
 
 
-def moe_gpu(q4k, banks, x, ids, wts, n_exp, hidden, inter):
+def moe_gpu(q4k, banks, x, ids, wts, n_exp, hidden, inter, bf16=False):
     m, top_k = ids.shape
     y = empty((m, hidden), torch.float32)
     ws = workspace(q4k, m, hidden, inter, top_k, 0)
     bg, bu, bd = banks
-    q4k.ffn_swiglu_q4k(dev(bg), dev(bu), dev(bd), dev(x), q4k.Q4K_F32, m, hidden, inter, y, ws,
-                       n_experts=n_exp, ids=dev(ids), wts=dev(wts), top_k=top_k)
+    xin = dev(synth.to_bf16_bits(x).view(np.int16)) if bf16 else dev(x)
+    q4k.ffn_swiglu_q4k(dev(bg), dev(bu), dev(bd), xin, q4k.Q4K_BF16 if bf16 else q4k.Q4K_F32, m,
+                       hidden, inter, y, ws, n_experts=n_exp, ids=dev(ids), wts=dev(wts),
+                       top_k=top_k)
     return host(y)
 
 
@@ -116,4 +129,20 @@ def test_moe_duplicates_and_out_of_range_ids(lib):
     valid = (ids >= 0) & (ids < n_exp)
     ref = orc.moe_decode(*banks, n_exp, hidden, inter, x, np.where(valid, ids, 0),
                          np.where(valid, wts, 0).astype(np.float32))
+    assert orc.relative_l2(y, ref) <= TOL
+
+
+@pytest.mark.parametrize("hidden,inter,bf16", [(4608, 512, False), (512, 4608, True)])
+def test_moe_wide_rows(lib, hidden, inter, bf16):
+    # rows that span wavefronts in the gate/up pass (hidden 4608) or the down
+    # pass (inter 4608); bf16 activations
+    say(f"moe wide rows {hidden}/{inter} bf16={bf16}")
+    n_exp, m, k = 3, 2, 2
+    banks = synth.moe_banks(94, n_exp, hidden, inter)
+    x = synth.activations(94, m, hidden, outliers=True)
+    ids = np.array([[2, 0], [0, 1]], dtype=np.int32)
+    wts = np.array([[0.75, 0.25], [0.5, 1.5]], dtype=np.float32)
+    y = moe_gpu(lib, banks, x, ids, wts, n_exp, hidden, inter, bf16=bf16)
+    xr = synth.bf16_bits_to_f32(synth.to_bf16_bits(x)) if bf16 else x
+    ref = orc.moe_decode(*banks, n_exp, hidden, inter, xr, ids, wts)
     assert orc.relative_l2(y, ref) <= TOL

@@ -36,6 +36,16 @@ def test_gemv_small(lib, m, n, k):
     check(lib, w, x, n, k)
 
 
+@pytest.mark.parametrize("m,n,k", [(3, 5000, 512), (8, 4200, 768), (5, 13000, 256), (2, 16, 32768)])
+def test_gemv_multi_token_tiles(lib, m, n, k):
+    # 2..8 tokens: two and three 16-row tiles per workgroup, four-wavefront
+    # workgroups once the grid exceeds the CUs (13000 rows), and the largest k
+    say(f"gemv tiles m={m} n={n} k={k}")
+    w = synth.random_q4k(synth.rng(72, 1, n + k), n, k)
+    x = synth.activations(72, m, k, outliers=True, sub=n)
+    check(lib, w, x, n, k)
+
+
 @pytest.mark.parametrize("shape", [0, 1, 2])
 def test_gemv_sweep_full_size(lib, shape):
     n, k, w, x = synth.gemv_sweep_case(shape)
