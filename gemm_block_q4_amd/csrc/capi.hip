@@ -274,9 +274,10 @@ int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int
   float* h = reinterpret_cast<float*>(ws + L.h);
 
   if (moe) {
-    // Every (token, slot) pair is an independent pass over its expert's
-    // rows: gate/up on x row t (h row = pair), down on h row = pair (pair
-    // output row), then the slot-order weighted combine.
+    // Gate/up: every (token, slot) pair is an independent pass over its
+    // expert's rows on x row t (h row = pair).  Down: per token, its slots'
+    // experts on the pairs' h rows, summed with the routing weights in slot
+    // order.
     GemvArgs gu{};
     gu.w = static_cast<const uint8_t*>(w_gate);
     gu.w_up = static_cast<const uint8_t*>(w_up);
@@ -304,11 +305,17 @@ int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int
     dn.x = h;
     dn.x_bf16 = 0;
     dn.ldx = inter;
-    dn.y = y_pair;
+    dn.y = y;
     dn.ldy = hidden;
     dn.n = hidden;
     dn.k = inter;
     dn.x_by_token = 0;
+    dn.wts = wts;
+    // down with the combine folded in when the rows fit one wavefront, else
+    // pair outputs and the combine kernel
+    e = launch_moe_down(dn, s);
+    if (e != hipErrorNotSupported) return launch_status(e);
+    dn.y = y_pair;
     if ((e = launch_gemv(dn, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
     return launch_status(launch_moe_combine(y_pair, wts, ids, m, top_k, n_experts, hidden, y, s));
   }

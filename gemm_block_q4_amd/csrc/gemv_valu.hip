@@ -492,6 +492,151 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
   }
 }
 
+// MoE down projection with the combine folded in.  Workgroup (row group, token
+// t) of W wavefronts; wavefront w takes slots w, w + W, ... of t.  For slot s
+// (pair p = t * top_k + s, expert ids[p]) the wavefront converts h row p into
+// its own LDS digits and runs the workgroup's rows of that expert (a row fits
+// one wavefront: k <= 4096); row results land in res[s][row].  Finally each
+// row adds wts[p] * res[s][row] over the valid slots in slot order
+// (deterministic) and writes y[t][row].  No pair buffer and no combine pass.
+template <int LAYOUT, int XU>
+__global__ __launch_bounds__(kThreadsMax) void moe_down_kernel(GemvArgs a, Geo geo) {
+  constexpr bool SEG64 = LAYOUT != kNarrow;
+  constexpr int PF = 4;
+  extern __shared__ __attribute__((aligned(16))) uint32_t smem_u[];
+  const int K = a.k >> 8;
+  const int S = 4 * K;
+  const int units = 4 * S;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nthr = geo.waves * 64;
+  const int t = blockIdx.y;
+  const int row0 = blockIdx.x * geo.rows;
+  const int rows = min(geo.rows, a.n - row0);
+  const uint32_t wbytes = static_cast<uint32_t>(rows) * static_cast<uint32_t>(K) * kBlockBytes;
+
+  // per-wavefront digits, then res[top_k][geo.rows]
+  uint32_t* dig = smem_u + static_cast<size_t>(wave) * x_words(S);
+  float* xinfo = reinterpret_cast<float*>(dig + static_cast<size_t>(S) * 48);
+  float* res = reinterpret_cast<float*>(smem_u + static_cast<size_t>(geo.waves) * x_words(S));
+
+  const int rslot = lane >> geo.lpr_log;  // row within a step (geo.rpw rows per step)
+  const int slice = lane & ((1 << geo.lpr_log) - 1);
+  const bool lane_ok = slice < S;
+  const int b = lane_ok ? slice >> 2 : 0;
+  const int g = lane & 3;
+  FieldSel fsel;
+  fsel.sh = 8u * static_cast<uint32_t>((2 * g) & 3);
+  fsel.upper = g >= 2;
+  const int seg_mask = SEG64 ? 63 : (1 << geo.lpr_log) - 1;
+  const int step = geo.rpw;  // rows per wavefront step
+  auto uni = [](int v) -> int {
+    int r;
+    asm("s_mov_b32 %0, %1" : "=s"(r) : "s"(v));
+    return r;
+  };
+  const uint32_t stride = static_cast<uint32_t>(step * K) * kBlockBytes;
+  const uint32_t base = static_cast<uint32_t>(rslot * K + b) * kBlockBytes;
+  auto step_off = [&](int it, uint32_t off) -> uint32_t {
+    return lane_ok && rslot < rows - uni(it * step) ? off : kOob;
+  };
+
+  for (int sl = wave; sl < a.top_k; sl += geo.waves) {  // uniform in the wavefront
+    const int pr = t * a.top_k + sl;
+    const int e = a.ids[pr];
+    if (e < 0 || e >= a.n_experts) continue;  // skipped again in the sum
+    const size_t wofs = static_cast<size_t>(e) * a.mat_bytes + static_cast<size_t>(row0) * K * kBlockBytes;
+    const rsrc_t rg = make_rsrc(a.w + wofs, wbytes);
+    const rsrc_t rx = make_rsrc(static_cast<const float*>(a.x) + static_cast<size_t>(pr) * a.ldx, 4u * a.k);
+    // 1. this lane's activation units (XU * 64 >= units), then the weights
+    float4 xr[XU][4];
+#pragma unroll
+    for (int j = 0; j < XU; ++j) {
+      const int u = lane + 64 * j;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        xr[j][c] = load_x4<false>(rx, u < units ? static_cast<uint32_t>(16 * u + 4 * c) : kOob);
+    }
+    RawSlice sg[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p)
+      load_slice(rg, step_off(p, base + static_cast<uint32_t>(uni(p * static_cast<int>(stride)))), g, sg[p]);
+    // 2. digits of h row pr in this wavefront's LDS (the wavefront's own
+    //    writes: complete at lgkmcnt(0))
+#pragma unroll
+    for (int j = 0; j < XU; ++j) {
+      const int u = lane + 64 * j;
+      convert_unit(xr[j], u, u < units, dig, xinfo);
+    }
+    __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    XSlice xs;
+    {
+      const uint32_t* dbase = dig + static_cast<size_t>(lane_ok ? slice : 0) * 48;
+#pragma unroll
+      for (int d = 0; d < 3; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 t4 = *reinterpret_cast<const uint4*>(dbase + 16 * d + 4 * i);
+          xs.dg[d][4 * i] = t4.x; xs.dg[d][4 * i + 1] = t4.y;
+          xs.dg[d][4 * i + 2] = t4.z; xs.dg[d][4 * i + 3] = t4.w;
+        }
+      const float4 inf = *reinterpret_cast<const float4*>(xinfo + 4 * (lane_ok ? slice : 0));
+      xs.scale = inf.x; xs.sum0 = inf.y; xs.sum1 = inf.z;
+    }
+    // 3. the workgroup's rows of expert e, PF steps in flight
+    float* rs = res + static_cast<size_t>(sl) * geo.rows;
+    auto finish = [&](float (&o)[PF], int it0) {
+#pragma unroll
+      for (int p = 0; p < PF; ++p) o[p] = SEG64 ? segment_sum<64>(o[p]) : segment_sum_rt(o[p], seg_mask + 1);
+#pragma unroll
+      for (int p = 0; p < PF; ++p) {
+        const int r = uni((it0 + p) * step) + rslot;
+        if (r < rows && (lane & seg_mask) == seg_mask) rs[r] = o[p];
+      }
+    };
+    auto dot = [&](const RawSlice& raw, bool ok) -> float {
+      const float v = slice_dot(expand(raw), fsel, xs);
+      return ok ? v : 0.f;
+    };
+    int it0 = 0;
+    uint32_t next = base + PF * stride;
+    for (; (it0 + PF) * step < rows; it0 += PF, next += PF * stride) {
+      float o[PF];
+#pragma unroll
+      for (int p = 0; p < PF; ++p) {
+        o[p] = dot(sg[p], lane_ok && rslot < rows - uni((it0 + p) * step));
+        load_slice(rg, step_off(it0 + p + PF, next + static_cast<uint32_t>(uni(p * static_cast<int>(stride)))), g, sg[p]);
+      }
+      finish(o, it0);
+    }
+    {
+      float o[PF];
+#pragma unroll
+      for (int p = 0; p < PF; ++p) {
+        o[p] = 0.f;
+        if ((it0 + p) * step < rows) o[p] = dot(sg[p], lane_ok && rslot < rows - uni((it0 + p) * step));
+      }
+      finish(o, it0);
+    }
+    // this wavefront's digits are rewritten by its next slot: its lanes are
+    // done reading them (registers) once the loop above has run
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+  // 4. y[t][row] = sum over valid slots, in slot order
+  for (int r = tid; r < rows; r += nthr) {
+    float acc = 0.f;
+    for (int sl = 0; sl < a.top_k; ++sl) {
+      const int pr = t * a.top_k + sl;
+      const int e = a.ids[pr];
+      if (e >= 0 && e < a.n_experts) acc = fmaf(a.wts[pr], res[static_cast<size_t>(sl) * geo.rows + r], acc);
+    }
+    a.y[static_cast<size_t>(t) * a.ldy + row0 + r] = acc;
+  }
+}
+
 // LDS bytes: digits and slice info, and the row partials when a row spans
 // wavefronts.
 size_t lds_bytes(const Geo& geo, int k, bool gu) {
@@ -600,6 +745,51 @@ hipError_t launch_d4(const GemvArgs& a, hipStream_t stream) {
 // at most 8 wavefronts per row, and the digits of all activations (208 bytes
 // per 64 values, 104 KiB at k = 32768) fit in LDS.
 bool gemv_valu_fits(int m, int k) { return m == 1 && k <= 32768; }
+
+// MoE down projection with the combine (rows that fit one wavefront, and the
+// per-wavefront digits and per-slot row results within LDS);
+// hipErrorNotSupported otherwise.
+hipError_t launch_moe_down(const GemvArgs& a, hipStream_t stream) {
+  constexpr int PF = 4;
+  const int K = a.k / kQK;
+  const int l = 4 * K;
+  if (l > 64 || a.w_up != nullptr || a.x_bf16 || a.top_k < 1) return hipErrorNotSupported;
+  Geo g{};
+  g.lpr = 1;
+  while (g.lpr < l) {
+    g.lpr <<= 1;
+    ++g.lpr_log;
+  }
+  g.wr = 1;
+  g.rpw = 64 / g.lpr;
+  g.waves = std::min(a.top_k, 8);
+  g.step = g.rpw;
+  g.rows = g.rpw * PF * 2;  // two prefetch groups per slot: one conversion serves more rows
+  const size_t lds = (static_cast<size_t>(g.waves) * x_words(l) +
+                      static_cast<size_t>(a.top_k) * g.rows) * sizeof(uint32_t);
+  if (lds > kLdsMax) return hipErrorNotSupported;
+  const int xu = (16 * K + 63) / 64;  // activation units per lane (1..4)
+  const dim3 grid((a.n + g.rows - 1) / g.rows, a.m);
+  auto go = [&](auto kern) -> hipError_t {
+    static bool big_lds = false;
+    if (lds > 64 * 1024 && !big_lds) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               static_cast<int>(kLdsMax));
+      if (e != hipSuccess) return e;
+      big_lds = true;
+    }
+    kern<<<grid, dim3(g.waves * 64), lds, stream>>>(a, g);
+    return hipGetLastError();
+  };
+  const bool one = g.lpr == 64;
+  switch (xu) {
+    case 1: return one ? go(moe_down_kernel<kOneWave, 1>) : go(moe_down_kernel<kNarrow, 1>);
+    case 2: return one ? go(moe_down_kernel<kOneWave, 2>) : go(moe_down_kernel<kNarrow, 2>);
+    case 3: return one ? go(moe_down_kernel<kOneWave, 3>) : go(moe_down_kernel<kNarrow, 3>);
+    default: return one ? go(moe_down_kernel<kOneWave, 4>) : go(moe_down_kernel<kNarrow, 4>);
+  }
+}
 
 hipError_t launch_gemv_valu(const GemvArgs& a, hipStream_t stream) {
   const bool gu = a.w_up != nullptr;

@@ -28,6 +28,7 @@ struct GemvArgs {
   // row p / top_k (x_by_token) or p and writes y row p.  Ids outside
   // [0, n_experts) are skipped.
   const int32_t* ids;
+  const float* wts;  // routing weights (the fused down pass)
   int x_by_token;
   int top_k;
   int n_experts;
@@ -38,6 +39,10 @@ struct GemvArgs {
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);
 hipError_t launch_gemv_valu(const GemvArgs& a, hipStream_t stream);
 hipError_t launch_gemv_mfma(const GemvArgs& a, hipStream_t stream);
+// MoE down projection on h rows (x = h [pairs][k], x_by_token = 0) with the
+// slot-order combine folded in: writes y[t] for every token.  Needs rows that
+// fit one wavefront (k <= 4096); hipErrorNotSupported otherwise.
+hipError_t launch_moe_down(const GemvArgs& a, hipStream_t stream);
 
 hipError_t launch_q8_1_quantize(const void* x, int x_bf16, int m, int k, int8_t* qs,
                                 uint32_t* ds, hipStream_t stream);
