@@ -53,10 +53,11 @@ constexpr int kWavesMax = 8;  // wavefronts per workgroup: 4, or 8 when the work
 constexpr int kRows = 16;  // output rows per workgroup (MFMA N)
 
 // Tokens per half of the activation operand (4 or 8), and blocks converted
-// per LDS round (the chunk's activation loads, MT * CH float4 per lane, stay
-// within 64 registers).
+// per LDS round.  Two blocks per chunk: a wavefront often owns only two blocks
+// of k (k = 4096 over 8 wavefronts), and a larger chunk then loads zeros for
+// the rest; one block per chunk leaves too little in flight.
 template <int MT> constexpr int half_rows() { return MT <= 4 ? 4 : 8; }
-template <int MT> constexpr int chunk_blocks() { return MT <= 4 ? 4 : 2; }
+template <int MT> constexpr int chunk_blocks() { return 2; }
 
 // LDS of one wavefront's activation operands for a chunk, R2 = 2 * half_rows:
 //   op: [CH][8 steps][4 lane groups][R2 rows] x 8 halves (16 B per entry);
