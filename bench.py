@@ -36,10 +36,10 @@ ROTATE_BYTES = 1 << 30         # per rotated tensor set
 # WRITE_SIZE (each scaled by what it reads for a copy of known size; summary and commands in
 # profiles/gemv_d4_decode_sweep_hbm_traffic.md) for the kernel sources with these SHA-256
 # digests.  Reported only while the sources still match.
-TRAFFIC_SWEEP_BYTES = 61266575
+TRAFFIC_SWEEP_BYTES = 61279864
 TRAFFIC_SOURCES = {
     "gemm_block_q4_amd/csrc/gemv_valu.hip":
-        "c3c6d1ca62c440a934ea02c250400c8146e4c8959c0b3056c3fad48c35f4cb1f",
+        "b481602cfe65f0ce5f37bc56e8fd0481ac6fc8644632773b09b00a1fa7a3949f",
     "gemm_block_q4_amd/csrc/q4k_device.hpp":
         "0ca9cfd803b914df0ad564490c5fd4e9deb5aaf1f4e89c866e6dd71f630d251d",
 }
