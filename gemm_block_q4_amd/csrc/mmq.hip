@@ -137,19 +137,21 @@ __device__ __forceinline__ LoadOffsets load_offsets(const MmqArgs& a, int K, int
 
 // Issues the staging loads of block b (all zeros when b == K: the last
 // iteration's prefetch).
+// The matrix of every staging load is uniform in the wavefront (weight chunk
+// load i serves LDS rows 64i .. 64i+63, i.e. matrix i of the fused pass; the
+// header load of wavefront w serves rows 64(w%2) .. +63), so the buffer
+// resource is picked without a per-lane select (which the compiler would
+// turn into a loop over the distinct resources).
 template <bool GU, bool PARTIALS>
 __device__ __forceinline__ void issue_loads(const LoadOffsets& o, rsrc_t rw0, rsrc_t rw1, rsrc_t rx,
-                                            rsrc_t rd, int K, int b, int tid, Loads& L) {
+                                            rsrc_t rd, int K, int b, int wave, Loads& L) {
   const bool live = b < K;  // uniform
   const uint32_t dw = static_cast<uint32_t>(b) * kBlockBytes;
   const uint32_t dx = static_cast<uint32_t>(b) * kQK;
   const uint32_t dd = static_cast<uint32_t>(b) * 32u;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int lr = (tid + i * kThreads) >> 3;
-    L.wq[i] = buf_load16(Geometry<GU>::matrix(lr) ? rw1 : rw0, live ? o.wq[i] + dw : kOob);
-  }
-  L.wh = buf_load16(Geometry<GU>::matrix(tid & 127) ? rw1 : rw0, live ? o.wh + dw : kOob);
+  for (int i = 0; i < 2; ++i) L.wq[i] = buf_load16(GU && i == 1 ? rw1 : rw0, live ? o.wq[i] + dw : kOob);
+  L.wh = buf_load16(GU && (wave & 1) ? rw1 : rw0, live ? o.wh + dw : kOob);
 #pragma unroll
   for (int i = 0; i < 4; ++i) L.xq[i] = buf_load16(rx, live ? o.xq[i] + dx : kOob);
   if constexpr (PARTIALS) {
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;  // wm 0..3: token tile; wn 0..1: weight half
   const int t0 = blockIdx.y * kBM;
   const int n0 = blockIdx.x * RPM;
@@ -273,13 +275,13 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
 
   const LoadOffsets lo = load_offsets<GU, PARTIALS>(a, K, nsub, rows, toks, tid);
   Loads L;
-  issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, K, 0, tid, L);
+  issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, K, 0, wave, L);
   store_stage<GU, PARTIALS>(stages[0], L, tid);
   __syncthreads();
 
   for (int b = 0; b < K; ++b) {
     // loads of the next block (zeros past the last one) fly during compute
-    issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, K, b + 1, tid, L);
+    issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, K, b + 1, wave, L);
     const Stage& S = stages[b & 1];
 #pragma unroll 1
     for (int p = 0; p < 4; ++p) {
