@@ -32,10 +32,11 @@
 // index 8*(l/16)+i of step s is weight 64*(l/16) + 8*s + i; the activation
 // operand uses the same K mapping.  Each wavefront converts its own
 // activation range a chunk of blocks at a time into LDS in operand layout.
-// Every global load is a raw buffer load (out-of-range lanes read zero), all
-// loads of a chunk are issued before any of them is used, and reductions
-// across lanes use DPP, so a chunk costs one memory latency.  The W partial
-// tiles are added in a fixed order at the end (deterministic).
+// Every global load is a raw buffer load (out-of-range lanes read zero); the
+// weights of the next tile (or of the next chunk's first tile) and the next
+// chunk's activations are in flight while the current ones are multiplied,
+// and reductions across lanes use DPP.  The W partial tiles are added in a
+// fixed order at the end (deterministic).
 #include <type_traits>
 
 #include "q4k_device.hpp"
