@@ -39,7 +39,7 @@ ROTATE_BYTES = 1 << 30         # per rotated tensor set
 TRAFFIC_SWEEP_BYTES = 61279864
 TRAFFIC_SOURCES = {
     "gemm_block_q4_amd/csrc/gemv_valu.hip":
-        "b481602cfe65f0ce5f37bc56e8fd0481ac6fc8644632773b09b00a1fa7a3949f",
+        "094eb220de80c4311a76906daa74afab5fc87a363c377b585b77aa182bab1b42",
     "gemm_block_q4_amd/csrc/q4k_device.hpp":
         "0ca9cfd803b914df0ad564490c5fd4e9deb5aaf1f4e89c866e6dd71f630d251d",
 }
