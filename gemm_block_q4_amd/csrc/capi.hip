@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 
 #include "../../include/q4k.h"
@@ -54,6 +55,21 @@ int check_device() {
     g_arch_ok[dev].store(state, std::memory_order_relaxed);
   }
   return state == 1 ? Q4K_OK : Q4K_ERR_DEVICE;
+}
+
+// Compute units of the current device (0 if unknown), cached per ordinal.
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int cus = g_cus[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      return 0;
+    g_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? Q4K_OK : Q4K_ERR_LAUNCH; }
@@ -374,7 +390,23 @@ int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int
   dn.m = m;
   dn.n = hidden;
   dn.k = inter;
-  return launch_status(launch_mmq(dn, s));
+  // When the down pass has too few workgroups to fill the device, split its
+  // k range; the partial sums go to the span of qx, dx and h, which nothing
+  // reads any more, and are added in split order.
+  const size_t plane = static_cast<size_t>(m) * static_cast<size_t>(hidden);
+  const int cus = device_cus();
+  const int max_splits = static_cast<int>(std::min<size_t>((L.qh - L.qx) / (plane * 4), 8));
+  const int splits = cus > 0 && max_splits > 1 && aligned(y, 16)  // the reduction stores float4
+                         ? mmq_choose_splits(m, hidden, inter, max_splits, cus)
+                         : 1;
+  if (splits == 1) return launch_status(launch_mmq(dn, s));
+  float* parts = reinterpret_cast<float*>(ws + L.qx);
+  dn.y = parts;
+  dn.splits = splits;
+  dn.split_blocks = (inter / Q4K_QK + splits - 1) / splits;
+  dn.split_stride = plane;
+  if ((e = launch_mmq(dn, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
+  return launch_status(launch_mmq_split_reduce(parts, splits, plane, plane, y, s));
 }
 
 }  // extern "C"

@@ -135,7 +135,7 @@ __device__ __forceinline__ LoadOffsets load_offsets(const MmqArgs& a, int K, int
   return o;
 }
 
-// Issues the staging loads of block b (all zeros when b == K: the last
+// Issues the staging loads of block b (all zeros when b == kend: the last
 // iteration's prefetch).
 // The matrix of every staging load is uniform in the wavefront (weight chunk
 // load i serves LDS rows 64i .. 64i+63, i.e. matrix i of the fused pass; the
@@ -144,8 +144,8 @@ __device__ __forceinline__ LoadOffsets load_offsets(const MmqArgs& a, int K, int
 // turn into a loop over the distinct resources).
 template <bool GU, bool PARTIALS>
 __device__ __forceinline__ void issue_loads(const LoadOffsets& o, rsrc_t rw0, rsrc_t rw1, rsrc_t rx,
-                                            rsrc_t rd, int K, int b, int wave, Loads& L) {
-  const bool live = b < K;  // uniform
+                                            rsrc_t rd, int kend, int b, int wave, Loads& L) {
+  const bool live = b < kend;  // uniform
   const uint32_t dw = static_cast<uint32_t>(b) * kBlockBytes;
   const uint32_t dx = static_cast<uint32_t>(b) * kQK;
   const uint32_t dd = static_cast<uint32_t>(b) * 32u;
@@ -273,16 +273,20 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) zf[i] = 0.f;
 
+  // this workgroup's k blocks: all of them, or split z of a k-split pass
+  const int kb0 = blockIdx.z * a.split_blocks;
+  const int kb1 = min(K, kb0 + a.split_blocks);
+
   const LoadOffsets lo = load_offsets<GU, PARTIALS>(a, K, nsub, rows, toks, tid);
   Loads L;
-  issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, K, 0, wave, L);
+  issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, kb1, kb0, wave, L);
   store_stage<GU, PARTIALS>(stages[0], L, tid);
   __syncthreads();
 
-  for (int b = 0; b < K; ++b) {
+  for (int b = kb0; b < kb1; ++b) {
     // loads of the next block (zeros past the last one) fly during compute
-    issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, K, b + 1, wave, L);
-    const Stage& S = stages[b & 1];
+    issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, kb1, b + 1, wave, L);
+    const Stage& S = stages[(b - kb0) & 1];
 #pragma unroll 1
     for (int p = 0; p < 4; ++p) {
       // weight fragments of sub-blocks 2p (low nibbles) and 2p+1 (high)
@@ -342,14 +346,14 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
     }
     // the other stage was last read in the previous iteration, before its
     // closing barrier
-    store_stage<GU, PARTIALS>(stages[(b + 1) & 1], L, tid);
+    store_stage<GU, PARTIALS>(stages[(b + 1 - kb0) & 1], L, tid);
     __syncthreads();
   }
 
   if constexpr (!PARTIALS) {
     // lane holds token xtok and, per tile, rows 8*(i/4) + 4*kh + i%4
     if (xtok < toks) {
-      float* yrow = a.y + static_cast<size_t>(t0 + xtok) * a.n;
+      float* yrow = a.y + blockIdx.z * a.split_stride + static_cast<size_t>(t0 + xtok) * a.n;
       if constexpr (GU) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -372,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
 template <bool GU, bool PARTIALS>
 hipError_t launch(const MmqArgs& a, hipStream_t stream) {
   constexpr int RPM = Geometry<GU>::kRowsPerMatrix;
-  const dim3 grid((a.n + RPM - 1) / RPM, (a.m + kBM - 1) / kBM);
+  const dim3 grid((a.n + RPM - 1) / RPM, (a.m + kBM - 1) / kBM, a.splits);
   const size_t lds = 2 * sizeof(Stage);
   auto kern = mmq_kernel<GU, PARTIALS>;
   static bool big_lds = false;  // the opt-in is per kernel and stays set
@@ -389,9 +393,70 @@ hipError_t launch(const MmqArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_mmq(const MmqArgs& a, hipStream_t stream) {
+hipError_t launch_mmq(const MmqArgs& args, hipStream_t stream) {
+  MmqArgs a = args;
+  const int K = a.k / kQK;
+  if (a.splits <= 1 || a.w_up || a.partials) {
+    a.splits = 1;
+    a.split_blocks = K;
+    a.split_stride = 0;
+  } else if (a.split_blocks < 1 || static_cast<long long>(a.splits - 1) * a.split_blocks >= K) {
+    return hipErrorInvalidValue;  // every split must own at least one block
+  }
   if (a.partials) return a.w_up ? launch<true, true>(a, stream) : launch<false, true>(a, stream);
   return a.w_up ? launch<true, false>(a, stream) : launch<false, false>(a, stream);
+}
+
+int mmq_choose_splits(int m, int n, int k, int max_splits, int cus) {
+  const long long tiles = static_cast<long long>((n + kWRows - 1) / kWRows) * ((m + kBM - 1) / kBM);
+  const int K = k / kQK;
+  int best = 1;
+  long long best_cost = -1;
+  for (int s = 1; s <= max_splits && s <= K; ++s) {
+    const int per = (K + s - 1) / s;
+    if ((s - 1) * per >= K) continue;  // an empty split
+    const long long rounds = (tiles * s + cus - 1) / cus;
+    const long long cost = rounds * per;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
+}
+
+namespace {
+
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ parts, int splits,
+                                                           size_t stride, size_t count4,
+                                                           float* __restrict__ y) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= count4) return;
+  const float4* p = reinterpret_cast<const float4*>(parts) + i;
+  const size_t s4 = stride / 4;
+  float4 acc = p[0];
+  for (int z = 1; z < splits; ++z) {
+    const float4 v = p[z * s4];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  reinterpret_cast<float4*>(y)[i] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_mmq_split_reduce(const float* parts, int splits, size_t stride, size_t count,
+                                   float* y, hipStream_t stream) {
+  if (splits < 1 || count % 4 || stride % 4 || (splits > 1 && stride < count)) return hipErrorInvalidValue;
+  const size_t count4 = count / 4;
+  if (count4 == 0) return hipSuccess;
+  const size_t blocks = (count4 + 255) / 256;
+  if (blocks > 0x7FFFFFFFu) return hipErrorInvalidValue;
+  split_reduce_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(parts, splits, stride,
+                                                                                     count4, y);
+  return hipGetLastError();
 }
 
 }  // namespace q4k

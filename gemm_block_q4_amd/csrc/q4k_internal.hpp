@@ -55,9 +55,26 @@ struct MmqArgs {
   float* y;              // [m][n] f32 (h = silu(g) * u when w_up is set)
   int32_t* partials;     // test hook: [m][n][k/32] int32 instead of y
   int m, n, k;
+  // k split of the single-matrix pass (splits > 1): split z covers k blocks
+  // [z * split_blocks, (z + 1) * split_blocks) and writes its partial sum to
+  // y + z * split_stride; mmq_split_reduce adds the planes.  splits <= 1:
+  // one pass over all of k into y.
+  int splits, split_blocks;
+  size_t split_stride;
 };
 
 hipError_t launch_mmq(const MmqArgs& a, hipStream_t stream);
+
+// Number of k splits (1 .. max_splits) for the single-matrix MMQ pass of an
+// m x n x k product on a device with `cus` compute units: the one that
+// minimises the busiest compute unit's share of k blocks (a workgroup fills a
+// compute unit), fewer splits on ties.
+int mmq_choose_splits(int m, int n, int k, int max_splits, int cus);
+
+// y[i] = sum_{z < splits} parts[z * stride + i] in order z = 0, 1, ...
+// (count and stride multiples of 4, 16-byte aligned planes).
+hipError_t launch_mmq_split_reduce(const float* parts, int splits, size_t stride, size_t count,
+                                   float* y, hipStream_t stream);
 
 // y[t] = sum_{s < top_k} wts[t][s] * y_pair[t * top_k + s] in slot order
 // (pairs with an id outside [0, n_experts) skipped).

@@ -57,6 +57,19 @@ def test_prefill_ffn_small(lib, m, regime):
     assert orc.relative_l2(y, ref) <= TOL
 
 
+@pytest.mark.parametrize("m,hidden,inter", [(300, 256, 2048), (130, 512, 1536), (200, 512, 768)])
+def test_prefill_ffn_k_split(lib, m, hidden, inter):
+    # inter >= 2 * hidden leaves room for the down pass's k-split partials
+    # (8 and 3 splits here); 512/768 has none and runs unsplit
+    say(f"ffn prefill k-split {hidden}/{inter} m={m}")
+    wg, wu, wd = synth.dense_ffn_weights(91, hidden, inter)
+    x = synth.activations(91, m, hidden, outliers=True, sub=m)
+    y = ffn_gpu(lib, wg, wu, wd, x, hidden, inter, regime=2, bf16=True)
+    xb = synth.bf16_bits_to_f32(synth.to_bf16_bits(x))
+    ref = orc.ffn_prefill(wg, wu, wd, hidden, inter, xb)
+    assert orc.relative_l2(y, ref) <= TOL
+
+
 @pytest.mark.parametrize("m,hidden,inter", [(1, 512, 768), (3, 512, 768), (6, 4608, 512)])
 def test_decode_ffn_bf16_input(lib, m, hidden, inter):
     # bf16 activations through the one-token and the matrix-core GEMVs
