@@ -96,7 +96,9 @@ struct FfnLayout {
   size_t total = 0;
   // decode dense (and MoE: h and the pair outputs of every (token, slot) pair)
   size_t h = 0, y_pair = 0;
-  // prefill
+  // prefill: Q8_1 of x and of h; the span qx .. qh (which includes h's
+  // m x inter f32 region, left unwritten) holds the down pass's k-split
+  // partial sums
   size_t qx = 0, dx = 0, qh = 0, dh = 0;
 };
 
@@ -364,7 +366,8 @@ int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int
     return launch_status(launch_gemv(dn, s));
   }
 
-  // Prefill: x -> Q8_1 -> MMQ gate/up with silu*mul -> h -> Q8_1 -> MMQ down.
+  // Prefill: x -> Q8_1 -> MMQ gate/up with silu*mul and Q8_1(h) in its
+  // epilogue -> MMQ down (h itself is never stored).
   int8_t* qx = reinterpret_cast<int8_t*>(ws + L.qx);
   uint32_t* dx = reinterpret_cast<uint32_t*>(ws + L.dx);
   int8_t* qh = reinterpret_cast<int8_t*>(ws + L.qh);
@@ -377,11 +380,12 @@ int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int
   gu.qs = qx;
   gu.ds = dx;
   gu.y = h;
+  gu.q_out = qh;
+  gu.d_out = dh;
   gu.m = m;
   gu.n = inter;
   gu.k = hidden;
   if ((e = launch_mmq(gu, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
-  if ((e = launch_q8_1_quantize(h, 0, m, inter, qh, dh, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
   MmqArgs dn{};
   dn.w = static_cast<const uint8_t*>(w_down);
   dn.qs = qh;
@@ -391,8 +395,8 @@ int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int
   dn.n = hidden;
   dn.k = inter;
   // When the down pass has too few workgroups to fill the device, split its
-  // k range; the partial sums go to the span of qx, dx and h, which nothing
-  // reads any more, and are added in split order.
+  // k range; the partial sums go to the span of qx, dx and h, which the down
+  // pass does not read, and are added in split order.
   const size_t plane = static_cast<size_t>(m) * static_cast<size_t>(hidden);
   const int cus = device_cus();
   const int max_splits = static_cast<int>(std::min<size_t>((L.qh - L.qx) / (plane * 4), 8));

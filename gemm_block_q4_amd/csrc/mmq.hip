@@ -35,6 +35,7 @@
 // zeros), issued for block b+1 before block b is computed.
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
+#include "q8_1_device.hpp"
 
 namespace q4k {
 
@@ -350,15 +351,49 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
     __syncthreads();
   }
 
+  if constexpr (GU && !PARTIALS) {
+    if (a.q_out != nullptr) {  // uniform
+      // Lanes l and l + 32 hold rows wn*32 + 8*(i/4) + 4*kh + i%4 of token
+      // xtok: together the 32 values of one Q8_1 block of h (n0 + wn*32 is a
+      // multiple of 32 and every row exists, n % 64 == 0).
+      float hv[16];
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        hv[i] = silu_mul(acc[0][i] - accm[0][i], acc[1][i] - accm[1][i]);
+        amax = fmaxf(amax, fabsf(hv[i]));
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      const float d = q8_1_scale(amax);
+      int q[16];
+      int s = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        q[i] = q8_1_quant(hv[i], amax, d);
+        s += q[i];
+      }
+      s += __shfl_xor(s, 32, 64);
+      if (xtok < toks) {
+        const size_t tok = static_cast<size_t>(t0 + xtok);
+        uint32_t* qrow = reinterpret_cast<uint32_t*>(a.q_out + tok * a.n + n0 + wn * 32);
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          qrow[2 * g4 + kh] = pack_q4(q[4 * g4], q[4 * g4 + 1], q[4 * g4 + 2], q[4 * g4 + 3]);
+        if (kh == 0) a.d_out[tok * (a.n / 32) + (n0 + wn * 32) / 32] = q8_1_word(amax, d, s);
+      }
+    }
+  }
   if constexpr (!PARTIALS) {
     // lane holds token xtok and, per tile, rows 8*(i/4) + 4*kh + i%4
     if (xtok < toks) {
       float* yrow = a.y + blockIdx.z * a.split_stride + static_cast<size_t>(t0 + xtok) * a.n;
       if constexpr (GU) {
+        if (a.q_out == nullptr) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = wn * 32 + 8 * (i >> 2) + 4 * kh + (i & 3);
-          if (r < rows) yrow[n0 + r] = silu_mul(acc[0][i] - accm[0][i], acc[1][i] - accm[1][i]);
+          for (int i = 0; i < 16; ++i) {
+            const int r = wn * 32 + 8 * (i >> 2) + 4 * kh + (i & 3);
+            if (r < rows) yrow[n0 + r] = silu_mul(acc[0][i] - accm[0][i], acc[1][i] - accm[1][i]);
+          }
         }
       } else {
 #pragma unroll
@@ -396,6 +431,7 @@ hipError_t launch(const MmqArgs& a, hipStream_t stream) {
 hipError_t launch_mmq(const MmqArgs& args, hipStream_t stream) {
   MmqArgs a = args;
   const int K = a.k / kQK;
+  if (a.q_out && (!a.w_up || !a.d_out || a.partials || a.n % 64)) return hipErrorInvalidValue;
   if (a.splits <= 1 || a.w_up || a.partials) {
     a.splits = 1;
     a.split_blocks = K;

@@ -53,6 +53,10 @@ struct MmqArgs {
   const int8_t* qs;      // Q8_1 quants [m][k]
   const uint32_t* ds;    // Q8_1 scale/sum words [m][k/32]
   float* y;              // [m][n] f32 (h = silu(g) * u when w_up is set)
+  // fused gate/up pass only (n % 64 == 0): h is quantised to Q8_1 in the
+  // epilogue into q_out [m][n] and d_out [m][n/32] instead of stored to y
+  int8_t* q_out;
+  uint32_t* d_out;
   int32_t* partials;     // test hook: [m][n][k/32] int32 instead of y
   int m, n, k;
   // k split of the single-matrix pass (splits > 1): split z covers k blocks

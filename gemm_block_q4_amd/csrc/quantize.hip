@@ -2,15 +2,15 @@
 //
 // "spark_model/layers/ops/q4k_mmq.rs", quantize_act_q8_1, and "realizar --
 // ffn.rs", fused_ffn_swiglu_gpu_true_dp4a (a per-block scale plus 32 int8
-// values; quantised once and shared by gate and up).  Per 32-value block:
-// amax = max |x|, d = amax / 127 in binary32, q = rint(x / d) (binary32
-// division, round half to even), stored d as binary16 (nearest even) and the
-// exact integer block sum S (a scale that would overflow binary16 saturates
-// at 65504 and quantises the block).  The kernel is memory-bound: one lane owns four
-// consecutive values, eight lanes (an aligned DPP row quarter) own a block and
-// combine their max and sum with three xor shuffles.
+// values; quantised once and shared by gate and up).  The per-block
+// arithmetic (q8_1_device.hpp): amax = max |x|, d = amax / 127 in binary32,
+// q = rint(x / d), d stored as binary16 next to the exact integer block sum.
+// The kernel is memory-bound: one lane owns four consecutive values, eight
+// lanes (an aligned DPP row quarter) own a block and combine their max and
+// sum with three xor shuffles.
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
+#include "q8_1_device.hpp"
 
 namespace q4k {
 
@@ -40,31 +40,17 @@ __global__ __launch_bounds__(256) void q8_1_quantize_kernel(const void* __restri
   amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
   amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
   amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
-  float d = amax / 127.0f;  // correctly rounded binary32 division
-  // A scale whose binary16 rounding would overflow saturates at the largest
-  // finite binary16 value, and the block is quantised with that stored scale.
-  if (d >= 65520.0f) d = 65504.0f;
+  const float d = q8_1_scale(amax);
   int q[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float r = amax > 0.0f ? rintf(v[j] / d) : 0.0f;
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    q[j] = static_cast<int>(r);
-  }
+  for (int j = 0; j < 4; ++j) q[j] = q8_1_quant(v[j], amax, d);
   int s = q[0] + q[1] + q[2] + q[3];
   s += __shfl_xor(s, 1, 64);
   s += __shfl_xor(s, 2, 64);
   s += __shfl_xor(s, 4, 64);
   if (valid) {
-    const uint32_t packed = (static_cast<uint32_t>(q[0]) & 0xFFu) |
-                            ((static_cast<uint32_t>(q[1]) & 0xFFu) << 8) |
-                            ((static_cast<uint32_t>(q[2]) & 0xFFu) << 16) |
-                            ((static_cast<uint32_t>(q[3]) & 0xFFu) << 24);
-    reinterpret_cast<uint32_t*>(qs)[i4] = packed;
-    if ((threadIdx.x & 7) == 0) {
-      const uint32_t dbits = amax > 0.0f ? float_to_half_bits(d) : 0u;
-      ds[i4 >> 3] = dbits | (static_cast<uint32_t>(static_cast<uint16_t>(static_cast<int16_t>(s))) << 16);
-    }
+    reinterpret_cast<uint32_t*>(qs)[i4] = pack_q4(q[0], q[1], q[2], q[3]);
+    if ((threadIdx.x & 7) == 0) ds[i4 >> 3] = q8_1_word(amax, d, s);
   }
 }
 
