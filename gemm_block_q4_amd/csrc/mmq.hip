@@ -30,9 +30,17 @@
 // Per 256-wide k block the workgroup stages, double-buffered in LDS, the raw
 // 144-byte weight blocks (their row stride keeps the fragment reads free of
 // bank conflicts), the 128 x 256 activation quants (row stride 272 bytes),
-// and per (row, sub-block) and (token, sub-block) the binary16 scale pieces.
+// and per (row, sub-block) and (token, sub-block) the bfloat16 scale pieces.
 // Global loads are raw buffer loads (rows past n and tokens past m read
 // zeros), issued for block b+1 before block b is computed.
+//
+// Epilogue modes: y (f32); for the fused gate/up pass either h = silu(g) * u
+// or, for the FFN, h quantised to Q8_1 on the spot (lanes l and l+32 hold one
+// 32-value block of a token, so its max and sum take one cross-half shuffle
+// each); for the single-matrix pass, optionally a split of the k blocks over
+// grid z, each split writing its own partial plane (added in order by
+// split_reduce_kernel), which fills the device when the row x token tiles
+// alone would leave compute units idle.
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
 #include "q8_1_device.hpp"
