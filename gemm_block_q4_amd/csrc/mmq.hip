@@ -14,11 +14,15 @@
 // vector, so they run on the matrix cores too, on exact bfloat16 pieces with
 // f32 accumulation (bfloat16 keeps the f32 exponent range, so saturated or
 // tiny scales are carried exactly):
-//  * cs = (d*sc)[n] * d_a[t]: d*sc (at most 17 significant bits) as three
-//    pieces, d_a (11 bits) as two: 6 K slots of v_mfma_f32_32x32x8_bf16;
+//  * cs = (d*sc)[n] * d_a[t], per sub-block: d*sc (at most 17 significant
+//    bits) as three pieces sw1..sw3, d_a (11 bits) as two, da1 and da2.  One
+//    v_mfma_f32_32x32x8_bf16 whose two K halves hold (sw1 sw2 sw3 0) against
+//    (da1 da1 da1 0) and (da2 da2 da2 0) sums the six exact piece products;
 //  * the min term (dmin*m)[n] * (d_a*S)[t]: three pieces each (d_a*S has at
-//    most 23 bits), 9 K slots of v_mfma_f32_32x32x16_bf16, accumulated over
-//    all sub-blocks in its own accumulator and subtracted at the end.
+//    most 23 bits).  Eight of the nine piece products (the dropped w3*x3 is
+//    below 2^-32 of the term) fill the eight K slots of one sub-block, so
+//    one v_mfma_f32_32x32x16_bf16 covers two sub-blocks; it accumulates over
+//    all of k in its own accumulator, subtracted at the end.
 // The vector ALUs then do one conversion and one FMA per output element and
 // sub-block: acc += cs * float(P).
 //
@@ -27,12 +31,17 @@
 // tokens x 64 weight rows (or 32 tokens x 32 rows of both matrices): two
 // 32x32 tiles.  Weight rows are the MFMA A operand (rows), tokens the B
 // operand (columns); lane l holds token l%32 and rows 8*(i/4) + 4*(l/32) + i%4.
-// Per 256-wide k block the workgroup stages, double-buffered in LDS, the raw
-// 144-byte weight blocks (their row stride keeps the fragment reads free of
-// bank conflicts), the 128 x 256 activation quants (row stride 272 bytes),
-// and per (row, sub-block) and (token, sub-block) the bfloat16 scale pieces.
-// Global loads are raw buffer loads (rows past n and tokens past m read
-// zeros), issued for block b+1 before block b is computed.
+//
+// Staging: per half block (128 k values, four sub-blocks), double-buffered
+// in LDS (64 KiB per stage), everything the inner loop reads is already in
+// MFMA operand form: the weight quants unpacked to one byte per weight, the
+// activation quants (both with a 144-byte row stride, free of bank
+// conflicts), and per (row, sub-block) and (token, sub-block) the bfloat16
+// scale pieces in the K-slot order of the two scale MFMAs.  The unpacking
+// and the scale splitting are done once per workgroup instead of in every
+// wavefront that reads them.  Global loads are raw buffer loads (rows past n
+// and tokens past m read zeros), issued for half block h+1 before half block
+// h is computed.
 //
 // Epilogue modes: y (f32); for the fused gate/up pass either h = silu(g) * u
 // or, for the FFN, h quantised to Q8_1 on the spot (lanes l and l+32 hold one
@@ -53,28 +62,30 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef short v4s __attribute__((ext_vector_type(4)));
-typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef uint32_t v8u32h __attribute__((ext_vector_type(4)));  // eight bfloat16 as four words
 
-constexpr int kBM = 128;          // tokens per workgroup
-constexpr int kWRows = 128;       // staged weight rows per workgroup (both matrices)
+constexpr int kBM = 128;                 // tokens per workgroup
+constexpr int kWRows = 128;              // staged weight rows per workgroup (both matrices)
 constexpr int kThreads = 512;
-constexpr int kXStride = kQK + 16;  // LDS row of activation quants (bytes)
+constexpr int kHalf = kQK / 2;           // k values per stage
+constexpr int kSubHalf = kHalf / kSub;   // sub-blocks per stage
+constexpr int kRowStride = kHalf + 16;   // LDS row of quants (bytes)
 
-// One LDS stage.  Scale records are three 32-bit words of bfloat16 pieces,
-// stored sub-block-major ([j][row], [j][token]: a 3-word stride between
-// lanes, free of bank conflicts):
-//   weights (row, sub-block): (sw1, sw2), (sw3, mw1), (mw2, mw3) for
-//     sw = d*sc and mw = dmin*m;
-//   tokens (token, sub-block): (da1, da2), (sa1, sa2), (sa3, 0) for d_a and
-//     sa = d_a*S.
+// One LDS stage.  bfloat16 pieces, two per 32-bit word (first K slot in the
+// low half):
+//   wc [sub-block][row]   (sw1 sw2, sw3 0)               cs, both K halves
+//   xc [sub-block][token] (da1 da1, da1 0 | da2 da2, da2 0) cs, K half 0 | 1
+//   wm [sub-block][row]   (w1 w1, w1 w2, w2 w2, w3 w3)   min, sw = d*sc,
+//   xm [sub-block][token] (x1 x2, x3 x1, x2 x3, x1 x2)   w = dmin*m, x = d_a*S
 struct Stage {
-  uint8_t w[kWRows * kBlockBytes];  // raw blocks, row stride 144
-  uint32_t ws[kWRows * 8 * 3];
-  uint8_t x[kBM * kXStride];        // activation quants, row stride 272
-  uint32_t xs[kBM * 8 * 3];
+  uint8_t w[kWRows * kRowStride];  // unpacked weight quants [row][128]
+  uint8_t x[kBM * kRowStride];     // activation quants [token][128]
+  uint2 wc[kSubHalf * kWRows];
+  uint4 xc[kSubHalf * kBM];
+  uint4 wm[kSubHalf * kWRows];
+  uint4 xm[kSubHalf * kBM];
 };
+static_assert(sizeof(Stage) == 65536, "stage layout");
 
 __device__ __forceinline__ uint32_t bf16_rne(float v) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(v)));
@@ -90,132 +101,131 @@ __device__ __forceinline__ void split3(float v, uint32_t& p1, uint32_t& p2, uint
   p3 = bf16_rne(r);
 }
 
-// Staging registers of one k block for one thread.
+// v = p1 + p2 exactly for v with at most 16 significant bits.
+__device__ __forceinline__ void split2(float v, uint32_t& p1, uint32_t& p2) {
+  p1 = bf16_rne(v);
+  p2 = bf16_rne(v - __uint_as_float(p1 << 16));
+}
+
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0);
+}
+
+// Staging registers of one half block for one thread.
 struct Loads {
-  uint4 wq[2];   // weight quant chunks
-  uint4 wh;      // weight header of row tid % 128
-  uint4 xq[4];   // activation quant chunks
-  uint2 xd;      // activation scale words: token tid % 128, sub-blocks 2*(tid/128) .. +1
+  uint4 wq;     // packed quants: LDS row tid / 4, 16-byte chunk tid % 4 of the half
+  uint4 wh;     // block header of LDS row tid % 128
+  uint4 xq[2];  // activation quant chunks
+  uint32_t xd;  // activation scale word: token tid % 128, sub-block tid / 128 of the half
 };
 
 template <bool GU>
 struct Geometry {
   // LDS weight row -> (matrix, row within the workgroup's rows)
-  __device__ static int matrix(int lr) { return GU ? lr >> 6 : 0; }
   __device__ static int row(int lr) { return GU ? (lr & 63) : lr; }
   static constexpr int kRowsPerMatrix = GU ? 64 : 128;
 };
 
-// Byte offsets of this thread's staging loads for block 0 (kOob for rows
-// past n, tokens past m, and the activation scales of the partials test hook,
-// which passes none); block b adds b * 144, b * 256 and b * 32.
+// Byte offsets of this thread's staging loads for half block 0 (kOob for
+// rows past n, tokens past m, and the activation scales of the partials test
+// hook, which passes none); half block hb = 2b + h adds b * 144 + 64h to the
+// quants, b * 144 to the header, 128 hb to the activations and 16 hb to the
+// scale words.
 struct LoadOffsets {
-  uint32_t wq[2], wh, xq[4], xd;
+  uint32_t wq, wh, xq[2], xd;
 };
 
 template <bool GU, bool PARTIALS>
 __device__ __forceinline__ LoadOffsets load_offsets(const MmqArgs& a, int K, int nsub, int rows,
                                                     int toks, int tid) {
   LoadOffsets o;
-  // weight quants: 128 rows x 8 chunks of 16 bytes; chunk c of row lr at
-  // byte 16 + 16c of the block
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int idx = tid + i * kThreads;
-    const int lr = idx >> 3, c = idx & 7;
+  {
+    const int lr = tid >> 2, c = tid & 3;
     const int r = Geometry<GU>::row(lr);
-    o.wq[i] = r < rows ? static_cast<uint32_t>(r * K) * kBlockBytes + 16u + 16u * c : kOob;
+    o.wq = r < rows ? static_cast<uint32_t>(r * K) * kBlockBytes + 16u + 16u * c : kOob;
   }
   {
     const int r = Geometry<GU>::row(tid & 127);
     o.wh = r < rows ? static_cast<uint32_t>(r * K) * kBlockBytes : kOob;
   }
-  // activation quants: 128 tokens x 16 chunks of 16 bytes
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
     const int idx = tid + i * kThreads;
-    const int t = idx >> 4, c = idx & 15;
+    const int t = idx >> 3, c = idx & 7;
     o.xq[i] = t < toks ? static_cast<uint32_t>(t) * a.k + 16u * c : kOob;
   }
   {
-    const int t = tid & 127, h = tid >> 7;
-    o.xd = !PARTIALS && t < toks ? (static_cast<uint32_t>(t) * nsub + 2 * h) * 4u : kOob;
+    const int t = tid & 127, jj = tid >> 7;
+    o.xd = !PARTIALS && t < toks ? (static_cast<uint32_t>(t) * nsub + jj) * 4u : kOob;
   }
   return o;
 }
 
-// Issues the staging loads of block b (all zeros when b == kend: the last
-// iteration's prefetch).
-// The matrix of every staging load is uniform in the wavefront (weight chunk
-// load i serves LDS rows 64i .. 64i+63, i.e. matrix i of the fused pass; the
-// header load of wavefront w serves rows 64(w%2) .. +63), so the buffer
-// resource is picked without a per-lane select (which the compiler would
-// turn into a loop over the distinct resources).
+// Issues the staging loads of half block hb (all zeros when hb == hend: the
+// last iteration's prefetch).  The matrix of every weight load is uniform in
+// the wavefront (quant chunks: LDS rows 16w .. 16w+15, i.e. matrix w / 4 of
+// the fused pass; headers: rows 64(w%2) .. +63), so the buffer resource is
+// picked without a per-lane select (which the compiler would turn into a
+// loop over the distinct resources).
 template <bool GU, bool PARTIALS>
 __device__ __forceinline__ void issue_loads(const LoadOffsets& o, rsrc_t rw0, rsrc_t rw1, rsrc_t rx,
-                                            rsrc_t rd, int kend, int b, int wave, Loads& L) {
-  const bool live = b < kend;  // uniform
-  const uint32_t dw = static_cast<uint32_t>(b) * kBlockBytes;
-  const uint32_t dx = static_cast<uint32_t>(b) * kQK;
-  const uint32_t dd = static_cast<uint32_t>(b) * 32u;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) L.wq[i] = buf_load16(GU && i == 1 ? rw1 : rw0, live ? o.wq[i] + dw : kOob);
+                                            rsrc_t rd, int hend, int hb, int wave, Loads& L) {
+  const bool live = hb < hend;  // uniform
+  const uint32_t dw = static_cast<uint32_t>(hb >> 1) * kBlockBytes;
+  const uint32_t dq = dw + static_cast<uint32_t>(hb & 1) * (kHalf / 2);
+  const uint32_t dx = static_cast<uint32_t>(hb) * kHalf;
+  const uint32_t dd = static_cast<uint32_t>(hb) * (kSubHalf * 4);
+  L.wq = buf_load16(GU && wave >= 4 ? rw1 : rw0, live ? o.wq + dq : kOob);
   L.wh = buf_load16(GU && (wave & 1) ? rw1 : rw0, live ? o.wh + dw : kOob);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) L.xq[i] = buf_load16(rx, live ? o.xq[i] + dx : kOob);
+  for (int i = 0; i < 2; ++i) L.xq[i] = buf_load16(rx, live ? o.xq[i] + dx : kOob);
   if constexpr (PARTIALS) {
-    L.xd = make_uint2(0u, 0u);
+    L.xd = 0u;
   } else {
-    L.xd = buf_load8(rd, live ? o.xd + dd : kOob);
+    L.xd = buf_load4(rd, live ? o.xd + dd : kOob);
   }
 }
 
 template <bool GU, bool PARTIALS>
-__device__ __forceinline__ void store_stage(Stage& S, const Loads& L, int tid) {
+__device__ __forceinline__ void store_stage(Stage& S, const Loads& L, int hb, int tid) {
+  // Quant chunk c of the half's 64 packed bytes: positions 16(c%2) .. +15 of
+  // sub-block 2(c/2) (low nibbles) and 2(c/2) + 1 (high nibbles).
+  {
+    const int lr = tid >> 2, c = tid & 3;
+    const int base = lr * kRowStride + 64 * (c >> 1) + 16 * (c & 1);
+    const uint4 v = L.wq;
+    *reinterpret_cast<uint4*>(&S.w[base]) =
+        make_uint4(v.x & 0x0F0F0F0Fu, v.y & 0x0F0F0F0Fu, v.z & 0x0F0F0F0Fu, v.w & 0x0F0F0F0Fu);
+    *reinterpret_cast<uint4*>(&S.w[base + kSub]) =
+        make_uint4((v.x >> 4) & 0x0F0F0F0Fu, (v.y >> 4) & 0x0F0F0F0Fu, (v.z >> 4) & 0x0F0F0F0Fu,
+                   (v.w >> 4) & 0x0F0F0F0Fu);
+  }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int idx = tid + i * kThreads;
-    const int lr = idx >> 3, c = idx & 7;
-    *reinterpret_cast<uint4*>(&S.w[lr * kBlockBytes + 16 + 16 * c]) = L.wq[i];
-  }
-  // weight scales: row tid % 128, sub-blocks 2*(tid/128) .. +1
-  {
-    const int lr = tid & 127, h = tid >> 7;
-    const float d = half_bits_to_float(L.wh.x & 0xFFFFu);
-    const float dmin = half_bits_to_float(L.wh.x >> 16);
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int j = 2 * h + jj;
-      uint32_t sc, mn, s1, s2, s3, m1, m2, m3;
-      scale_min_rt(L.wh, j, sc, mn);
-      split3(d * static_cast<float>(sc), s1, s2, s3);     // exact product
-      split3(dmin * static_cast<float>(mn), m1, m2, m3);
-      uint32_t* rec = &S.ws[(j * kWRows + lr) * 3];
-      rec[0] = s1 | (s2 << 16);
-      rec[1] = s3 | (m1 << 16);
-      rec[2] = m2 | (m3 << 16);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int idx = tid + i * kThreads;
-    const int t = idx >> 4, c = idx & 15;
-    *reinterpret_cast<uint4*>(&S.x[t * kXStride + 16 * c]) = L.xq[i];
+    const int t = idx >> 3, c = idx & 7;
+    *reinterpret_cast<uint4*>(&S.x[t * kRowStride + 16 * c]) = L.xq[i];
   }
   if constexpr (!PARTIALS) {
-    const int t = tid & 127, h = tid >> 7;
-    const uint32_t wd[2] = {L.xd.x, L.xd.y};
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const float da = half_bits_to_float(wd[jj] & 0xFFFFu);
-      const float sa = da * static_cast<float>(static_cast<int16_t>(wd[jj] >> 16));  // exact
-      uint32_t d1, d2, d3, a1, a2, a3;
-      split3(da, d1, d2, d3);  // d3 = 0: d_a has 11 significant bits
+    const int r = tid & 127, jj = tid >> 7;  // LDS row or token; sub-block of the half
+    {
+      const float d = half_bits_to_float(L.wh.x & 0xFFFFu);
+      const float dmin = half_bits_to_float(L.wh.x >> 16);
+      uint32_t sc, mn, s1, s2, s3, m1, m2, m3;
+      scale_min_rt(L.wh, 4 * (hb & 1) + jj, sc, mn);
+      split3(d * static_cast<float>(sc), s1, s2, s3);  // exact products
+      split3(dmin * static_cast<float>(mn), m1, m2, m3);
+      S.wc[jj * kWRows + r] = make_uint2(s1 | (s2 << 16), s3);
+      S.wm[jj * kWRows + r] = make_uint4(m1 | (m1 << 16), m1 | (m2 << 16), m2 | (m2 << 16), m3 | (m3 << 16));
+    }
+    {
+      const float da = half_bits_to_float(L.xd & 0xFFFFu);
+      const float sa = da * static_cast<float>(static_cast<int16_t>(L.xd >> 16));  // exact
+      uint32_t d1, d2, a1, a2, a3;
+      split2(da, d1, d2);
       split3(sa, a1, a2, a3);
-      uint32_t* rec = &S.xs[((2 * h + jj) * kBM + t) * 3];
-      rec[0] = d1 | (d2 << 16);
-      rec[1] = a1 | (a2 << 16);
-      rec[2] = a3;
+      S.xc[jj * kBM + r] = make_uint4(d1 | (d1 << 16), d1, d2 | (d2 << 16), d2);
+      S.xm[jj * kBM + r] = make_uint4(a1 | (a2 << 16), a3 | (a1 << 16), a2 | (a3 << 16), a1 | (a2 << 16));
     }
   }
 }
@@ -249,22 +259,7 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
 
   // this lane's operand rows: weight tile wt in {0, 1} -> LDS weight row
   const int r32 = lane & 31;
-  const int kh = lane >> 5;  // K half of the 32-wide operands / slot half of the K=8 ones
-  // v_perm selectors (bytes 0-3: second source, 4-7: first source, 0x0C: 0)
-  // that build this lane's half of the scale operands from the records
-  struct {
-    uint32_t c0, c1, m0, m1, m2, m3, b0, b1, b2, b3;
-  } sel;
-  if (kh == 0) {
-    sel = {0x01000100u, 0x03020302u,                              // (sw1 sw1) (sw2 sw2)
-           0x03020302u, 0x05040302u, 0x05040504u, 0x07060706u,    // (mw1 mw1) (mw1 mw2) (mw2 mw2) (mw3 mw3)
-           0x03020100u, 0x01000504u, 0x05040302u, 0x03020100u};   // (sa1 sa2) (sa3 sa1) (sa2 sa3) (sa1 sa2)
-  } else {
-    sel = {0x05040504u, 0x0C0C0C0Cu,                              // (sw3 sw3) (0 0)
-           0x0C0C0706u, 0x0C0C0C0Cu, 0x0C0C0C0Cu, 0x0C0C0C0Cu,    // (mw3 0) 0 0 0
-           0x0C0C0504u, 0x0C0C0C0Cu, 0x0C0C0C0Cu, 0x0C0C0C0Cu};   // (sa3 0) 0 0 0
-  }
-  const uint32_t lo_mask = kh == 0 ? 0xFFFFFFFFu : 0u;  // cs token slots 2, 3 live in the first half
+  const int kh = lane >> 5;  // K half of the MFMA operands
   int wrow[2];
 #pragma unroll
   for (int wt = 0; wt < 2; ++wt) wrow[wt] = GU ? wt * 64 + wn * 32 + r32 : wn * 64 + wt * 32 + r32;
@@ -282,80 +277,116 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) zf[i] = 0.f;
 
-  // this workgroup's k blocks: all of them, or split z of a k-split pass
+  // this workgroup's half blocks: all of k, or split z of a k-split pass
   const int kb0 = blockIdx.z * a.split_blocks;
   const int kb1 = min(K, kb0 + a.split_blocks);
+  const int hb0 = 2 * kb0, hb1 = 2 * kb1;
 
   const LoadOffsets lo = load_offsets<GU, PARTIALS>(a, K, nsub, rows, toks, tid);
-  Loads L;
-  issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, kb1, kb0, wave, L);
-  store_stage<GU, PARTIALS>(stages[0], L, tid);
-  __syncthreads();
-
-  for (int b = kb0; b < kb1; ++b) {
-    // loads of the next block (zeros past the last one) fly during compute
-    issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, kb1, b + 1, wave, L);
-    const Stage& S = stages[(b - kb0) & 1];
-#pragma unroll 1
-    for (int p = 0; p < 4; ++p) {
-      // weight fragments of sub-blocks 2p (low nibbles) and 2p+1 (high)
-      v4i wq[2];
+  // Staging loads run two half blocks ahead of the compute: L0 holds even
+  // half blocks, L1 odd ones, and the loop covers one whole block (two half
+  // blocks) per iteration so that both register sets keep fixed names.
+  // Global latency under load (weights come from HBM or the Infinity Cache)
+  // exceeds one half block of compute.
+  auto compute = [&](const Stage& S, int hb) {
+    __builtin_amdgcn_sched_barrier(0);
+    // Units u = 2*jj + wt (sub-block jj of the half, weight tile wt) run as a
+    // three-stage software pipeline inside the wavefront: while the VALU
+    // converts and scales unit u, the two MFMAs of unit u+1 are in flight and
+    // the LDS operands of unit u+2 are being read, so neither the LDS nor
+    // the matrix-core latency stalls the wavefront.
+    v4i av[2], xv[2];
+    v2u32 ca[2], cb[2];
+    v16i P[2];
+    v16f C[2];
+    uint4 mb, ma[2];
+    auto load_ops = [&](int u) {
+      const int jj = u >> 1, wt = u & 1;
+      if (wt == 0) {
+        xv[jj & 1] = *reinterpret_cast<const v4i*>(&S.x[xtok * kRowStride + kSub * jj + 16 * kh]);
+        if constexpr (!PARTIALS)
+          cb[jj & 1] =
+              *reinterpret_cast<const v2u32*>(reinterpret_cast<const uint8_t*>(&S.xc[jj * kBM + xtok]) + 8 * kh);
+      }
+      av[u & 1] = *reinterpret_cast<const v4i*>(&S.w[wrow[wt] * kRowStride + kSub * jj + 16 * kh]);
+      if constexpr (!PARTIALS) {
+        const uint2 c = S.wc[jj * kWRows + wrow[wt]];
+        ca[u & 1] = v2u32{c.x, c.y};
+      }
+    };
+    auto issue = [&](int u) {
+      const int jj = u >> 1;
+      P[u & 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[u & 1], xv[jj & 1], zi, 0, 0, 0);
+      if constexpr (!PARTIALS)
+        C[u & 1] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(v4s, ca[u & 1]),
+                                                             __builtin_bit_cast(v4s, cb[jj & 1]), zf, 0, 0, 0);
+    };
+    // min term: K half kh of MFMA i2 is sub-block 2*i2 + kh
+    auto load_min = [&](int i2) {
+      mb = S.xm[(2 * i2 + kh) * kBM + xtok];
+#pragma unroll
+      for (int wt = 0; wt < 2; ++wt) ma[wt] = S.wm[(2 * i2 + kh) * kWRows + wrow[wt]];
+    };
+    auto min_term = [&]() {
 #pragma unroll
       for (int wt = 0; wt < 2; ++wt)
-        wq[wt] = *reinterpret_cast<const v4i*>(&S.w[wrow[wt] * kBlockBytes + 16 + 32 * p + 16 * kh]);
+        accm[wt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ma[wt]),
+                                                            __builtin_bit_cast(v8bf, mb), accm[wt], 0, 0, 0);
+    };
+    constexpr int kUnits = 2 * kSubHalf;
+    load_ops(0);
+    load_ops(1);
+    issue(0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        const int j = 2 * p + hs;
-        const v4i xv = *reinterpret_cast<const v4i*>(&S.x[xtok * kXStride + 32 * j + 16 * kh]);
-        // scale operands: lanes 0..31 hold the first half of the K slots,
-        // lanes 32..63 the second; v_perm with per-lane selectors builds
-        // both halves without branches.
-        // token side: cs slots [da1 da2 da1 da2 | da1 da2 0 0],
-        // min slots [sa1 sa2 sa3 sa1 sa2 sa3 sa1 sa2 | sa3 0 ...]
-        v4u32 csb;
-        v8u32h mnb;
-        {
-          const uint32_t* rec = &S.xs[(j * kBM + xtok) * 3];
-          const uint32_t x0 = rec[0], x1 = rec[1], x2 = rec[2];
-          csb = v4u32{x0, x0 & lo_mask, 0u, 0u};
-          mnb = v8u32h{__builtin_amdgcn_perm(x2, x1, sel.b0), __builtin_amdgcn_perm(x2, x1, sel.b1),
-                       __builtin_amdgcn_perm(x2, x1, sel.b2), __builtin_amdgcn_perm(x2, x1, sel.b3)};
-        }
-#pragma unroll
-        for (int wt = 0; wt < 2; ++wt) {
-          const v4i av = hs == 0 ? (wq[wt] & 0x0F0F0F0F) : ((wq[wt] >> 4) & 0x0F0F0F0F);
-          const v16i P = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, xv, zi, 0, 0, 0);
-          if constexpr (PARTIALS) {
-            // C row i of this lane: weight row 8*(i/4) + 4*kh + i%4 of the tile
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int lr = (GU ? wt * 64 + wn * 32 : wn * 64 + wt * 32) + 8 * (i >> 2) + 4 * kh + (i & 3);
-              const int r = Geometry<GU>::row(lr);
-              if (r < rows && xtok < toks)
-                a.partials[(static_cast<size_t>(t0 + xtok) * a.n + n0 + r) * nsub + b * 8 + j] = P[i];
-            }
-          } else {
-            // weight side: cs slots [sw1 sw1 sw2 sw2 | sw3 sw3 0 0],
-            // min slots [mw1 mw1 mw1 mw2 mw2 mw2 mw3 mw3 | mw3 0 ...]
-            const uint32_t* rec = &S.ws[(j * kWRows + wrow[wt]) * 3];
-            const uint32_t w0 = rec[0], w1 = rec[1], w2 = rec[2];
-            const v2u32 csa = v2u32{__builtin_amdgcn_perm(w1, w0, sel.c0), __builtin_amdgcn_perm(w1, w0, sel.c1)};
-            const v4u32 mna = v4u32{__builtin_amdgcn_perm(w2, w1, sel.m0), __builtin_amdgcn_perm(w2, w1, sel.m1),
-                                    __builtin_amdgcn_perm(w2, w1, sel.m2), __builtin_amdgcn_perm(w2, w1, sel.m3)};
-            const v16f cs = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(__builtin_bit_cast(v4s, csa),
-                                                                      __builtin_bit_cast(v4s, v2u32{csb[0], csb[1]}),
-                                                                      zf, 0, 0, 0);
-            accm[wt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, mna),
-                                                                __builtin_bit_cast(v8bf, mnb), accm[wt], 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[wt][i] = fmaf(cs[i], static_cast<float>(P[i]), acc[wt][i]);
-          }
-        }
+    for (int u = 0; u < kUnits; ++u) {
+      const int jj = u >> 1, wt = u & 1;
+      const v16i Pu = P[u & 1];
+      const v16f Cu = C[u & 1];
+      if (u + 1 < kUnits) issue(u + 1);
+      if constexpr (!PARTIALS) {
+        if (u == 2 || u == 6) min_term();
       }
+      if (u + 2 < kUnits) load_ops(u + 2);
+      if constexpr (!PARTIALS) {
+        if (u == 0 || u == 4) load_min(u / 4);
+      }
+      // fence: the scheduler keeps each pipeline step in this order
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (PARTIALS) {
+        // C row i of this lane: weight row 8*(i/4) + 4*kh + i%4 of the tile
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int lr = (GU ? wt * 64 + wn * 32 : wn * 64 + wt * 32) + 8 * (i >> 2) + 4 * kh + (i & 3);
+          const int r = Geometry<GU>::row(lr);
+          if (r < rows && xtok < toks)
+            a.partials[(static_cast<size_t>(t0 + xtok) * a.n + n0 + r) * nsub + kSubHalf * hb + jj] = Pu[i];
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[wt][i] = fmaf(Cu[i], static_cast<float>(Pu[i]), acc[wt][i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // the other stage was last read in the previous iteration, before its
-    // closing barrier
-    store_stage<GU, PARTIALS>(stages[(b + 1 - kb0) & 1], L, tid);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  Loads L0, L1;
+  issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, hb1, hb0, wave, L0);
+  store_stage<GU, PARTIALS>(stages[0], L0, hb0, tid);
+  issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, hb1, hb0 + 1, wave, L1);
+  issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, hb1, hb0 + 2, wave, L0);
+  __syncthreads();
+
+  for (int hb = hb0; hb < hb1; hb += 2) {
+    // stage 1 was last read in the previous iteration, before its closing
+    // barrier; stage 0 in the first half of this one
+    compute(stages[0], hb);
+    store_stage<GU, PARTIALS>(stages[1], L1, hb + 1, tid);
+    issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, hb1, hb + 3, wave, L1);
+    __syncthreads();
+    compute(stages[1], hb + 1);
+    store_stage<GU, PARTIALS>(stages[0], L0, hb + 2, tid);
+    issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, hb1, hb + 4, wave, L0);
     __syncthreads();
   }
 
