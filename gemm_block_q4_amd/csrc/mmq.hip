@@ -170,24 +170,47 @@ __device__ __forceinline__ LoadOffsets load_offsets(const MmqArgs& a, int K, int
 template <bool GU, bool PARTIALS>
 __device__ __forceinline__ void issue_loads(const LoadOffsets& o, rsrc_t rw0, rsrc_t rw1, rsrc_t rx,
                                             rsrc_t rd, int hend, int hb, int wave, Loads& L) {
-  const bool live = hb < hend;  // uniform
-  const uint32_t dw = static_cast<uint32_t>(hb >> 1) * kBlockBytes;
-  const uint32_t dq = dw + static_cast<uint32_t>(hb & 1) * (kHalf / 2);
-  const uint32_t dx = static_cast<uint32_t>(hb) * kHalf;
-  const uint32_t dd = static_cast<uint32_t>(hb) * (kSubHalf * 4);
-  L.wq = buf_load16(GU && wave >= 4 ? rw1 : rw0, live ? o.wq + dq : kOob);
-  L.wh = buf_load16(GU && (wave & 1) ? rw1 : rw0, live ? o.wh + dw : kOob);
+  // Uniform deltas; past the end every delta is kDead, which puts each
+  // offset (at most kOob plus a real delta) at or above every resource's
+  // size without wrapping, so those loads read zeros.
+  constexpr uint32_t kDead = 0x40000000u;
+  const bool live = hb < hend;
+  const uint32_t dw = live ? static_cast<uint32_t>(hb >> 1) * kBlockBytes : kDead;
+  const uint32_t dq = live ? dw + static_cast<uint32_t>(hb & 1) * (kHalf / 2) : kDead;
+  const uint32_t dx = live ? static_cast<uint32_t>(hb) * kHalf : kDead;
+  const uint32_t dd = live ? static_cast<uint32_t>(hb) * (kSubHalf * 4) : kDead;
+  L.wq = buf_load16(GU && wave >= 4 ? rw1 : rw0, o.wq + dq);
+  L.wh = buf_load16(GU && (wave & 1) ? rw1 : rw0, o.wh + dw);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) L.xq[i] = buf_load16(rx, live ? o.xq[i] + dx : kOob);
+  for (int i = 0; i < 2; ++i) L.xq[i] = buf_load16(rx, o.xq[i] + dx);
   if constexpr (PARTIALS) {
     L.xd = 0u;
   } else {
-    L.xd = buf_load4(rd, live ? o.xd + dd : kOob);
+    L.xd = buf_load4(rd, o.xd + dd);
   }
 }
 
-template <bool GU, bool PARTIALS>
-__device__ __forceinline__ void store_stage(Stage& S, const Loads& L, int hb, int tid) {
+// 6-bit scale and min of sub-block 4H + u of a block header (u uniform,
+// 0..3): for the first half, the low 6 bits of scales[u] and scales[u+4];
+// for the second, the low and high nibbles of scales[u+8] below the top two
+// bits of scales[u] (scale) and scales[u+4] (min).
+template <int H>
+__device__ __forceinline__ void scale_min_half(const uint4& h, int u, uint32_t& sc, uint32_t& mn) {
+  const int sh = 8 * u;
+  if constexpr (H == 0) {
+    sc = (h.y >> sh) & 63u;
+    mn = (h.z >> sh) & 63u;
+  } else {
+    const uint32_t b1 = h.y >> sh, b2 = h.z >> sh, b3 = h.w >> sh;
+    sc = (b3 & 15u) | ((b1 >> 2) & 48u);
+    mn = ((b3 >> 4) & 15u) | ((b2 >> 2) & 48u);
+  }
+}
+
+// Writes the stage of a half block with parity H (quants of bytes 64H ..
+// 64H+63 of each block's quant field, sub-blocks 4H .. 4H+3).
+template <bool GU, bool PARTIALS, int H>
+__device__ __forceinline__ void store_stage(Stage& S, const Loads& L, int wave, int tid) {
   // Quant chunk c of the half's 64 packed bytes: positions 16(c%2) .. +15 of
   // sub-block 2(c/2) (low nibbles) and 2(c/2) + 1 (high nibbles).
   {
@@ -207,12 +230,12 @@ __device__ __forceinline__ void store_stage(Stage& S, const Loads& L, int hb, in
     *reinterpret_cast<uint4*>(&S.x[t * kRowStride + 16 * c]) = L.xq[i];
   }
   if constexpr (!PARTIALS) {
-    const int r = tid & 127, jj = tid >> 7;  // LDS row or token; sub-block of the half
+    const int r = tid & 127, jj = wave >> 1;  // LDS row or token; sub-block of the half (uniform)
     {
       const float d = half_bits_to_float(L.wh.x & 0xFFFFu);
       const float dmin = half_bits_to_float(L.wh.x >> 16);
       uint32_t sc, mn, s1, s2, s3, m1, m2, m3;
-      scale_min_rt(L.wh, 4 * (hb & 1) + jj, sc, mn);
+      scale_min_half<H>(L.wh, jj, sc, mn);
       split3(d * static_cast<float>(sc), s1, s2, s3);  // exact products
       split3(dmin * static_cast<float>(mn), m1, m2, m3);
       S.wc[jj * kWRows + r] = make_uint2(s1 | (s2 << 16), s3);
@@ -372,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
   };
   Loads L0, L1;
   issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, hb1, hb0, wave, L0);
-  store_stage<GU, PARTIALS>(stages[0], L0, hb0, tid);
+  store_stage<GU, PARTIALS, 0>(stages[0], L0, wave, tid);
   issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, hb1, hb0 + 1, wave, L1);
   issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, hb1, hb0 + 2, wave, L0);
   __syncthreads();
@@ -381,11 +404,11 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
     // stage 1 was last read in the previous iteration, before its closing
     // barrier; stage 0 in the first half of this one
     compute(stages[0], hb);
-    store_stage<GU, PARTIALS>(stages[1], L1, hb + 1, tid);
+    store_stage<GU, PARTIALS, 1>(stages[1], L1, wave, tid);
     issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, hb1, hb + 3, wave, L1);
     __syncthreads();
     compute(stages[1], hb + 1);
-    store_stage<GU, PARTIALS>(stages[0], L0, hb + 2, tid);
+    store_stage<GU, PARTIALS, 0>(stages[0], L0, wave, tid);
     issue_loads<GU, PARTIALS>(lo, rw0, rw1, rx, rd, hb1, hb + 4, wave, L0);
     __syncthreads();
   }
