@@ -81,3 +81,16 @@ def test_mmq_prefill_gate_full_size(lib):
     y1 = check(lib, w, qs, d16, s, n, k, tokens=[0, 63, 64, 300, 511])
     y2 = mmq_gpu(lib, w, qs, d16, s, n, k)
     assert np.array_equal(y1, y2)
+
+
+def test_mmq_max_k(lib):
+    # the largest k the prefill path accepts (2^20): the staging offsets of the
+    # last blocks and the past-the-end prefetch stay inside 32 bits
+    m, n, k = 2, 3, 1 << 20
+    say(f"mmq max k m={m} n={n} k={k}")
+    w = synth.random_q4k(synth.rng(85, 1), n, k)
+    qs, d16, s = quantised(m, k, 9)
+    check(lib, w, qs, d16, s, n, k)
+    p = empty((m, n, k // 32), torch.int32)
+    lib.q4k_test_mmq_partials(dev(w), dev(qs), m, n, k, p)
+    assert np.array_equal(host(p).astype(np.int64), orc.mmq_partials(w, n, k, qs))
