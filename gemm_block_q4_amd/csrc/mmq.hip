@@ -374,9 +374,9 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
       if constexpr (!PARTIALS) {
         if (u == 0 || u == 4) load_min(u / 4);
       }
-      // fence: the scheduler keeps each pipeline step in this order
-      __builtin_amdgcn_sched_barrier(0);
       if constexpr (PARTIALS) {
+        // fence: the scheduler keeps each pipeline step in this order
+        __builtin_amdgcn_sched_barrier(0);
         // C row i of this lane: weight row 8*(i/4) + 4*kh + i%4 of the tile
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -388,6 +388,17 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[wt][i] = fmaf(Cu[i], static_cast<float>(Pu[i]), acc[wt][i]);
+        // The step's MFMAs (unit u+1, min term) and LDS reads (unit u+2) do
+        // not depend on its VALU work (unit u): spread them through it, so a
+        // wavefront issues them while the SIMD's VALU runs the other
+        // wavefront's instructions instead of both stalling the VALU at once.
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
