@@ -38,6 +38,7 @@ _SIGNATURES = {
     "q8_1_quantize": (_I, [_VP, _I, _I, _I, _VP, _VP, _VP]),
     "q4k_mmq": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _VP]),
     "q4k_test_mmq_partials": (_I, [_VP, _VP, _I, _I, _I, _VP, _VP]),
+    "q4k_q8_gemv": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _VP]),
     "ffn_swiglu_q4k_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "ffn_swiglu_q4k": (_I, [_VP, _VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP, _I, _I, _VP,
                             _VP, _SZ, _VP]),
@@ -111,6 +112,12 @@ def q8_1_quantize(x, x_dtype: int, m: int, k: int, qs, ds, stream=None) -> None:
 def q4k_mmq(w, qs, ds, y, m: int, n: int, k: int, stream=None) -> None:
     _check(load_library().q4k_mmq(_ptr(w), _ptr(qs), _ptr(ds), _ptr(y), m, n, k,
                                   _stream(stream)))
+
+
+def q4k_q8_gemv(w, qs, ds, y, m: int, n: int, k: int, stream=None) -> None:
+    """y[m, n] = reference dot of Q8_1 rows (qs, ds) with the Q4_K rows, m <= 8."""
+    _check(load_library().q4k_q8_gemv(_ptr(w), _ptr(qs), _ptr(ds), _ptr(y), m, n, k,
+                                      _stream(stream)))
 
 
 def q4k_test_mmq_partials(w, qs, m: int, n: int, k: int, partials, stream=None) -> None:

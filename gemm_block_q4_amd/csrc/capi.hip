@@ -234,6 +234,20 @@ int q4k_mmq(const void* w, const int8_t* qs, const uint32_t* ds, float* y, int m
   return mmq_common(w, qs, ds, y, nullptr, m, n, k, stream);
 }
 
+int q4k_q8_gemv(const void* w, const int8_t* qs, const uint32_t* ds, float* y, int m, int n, int k,
+                void* stream) {
+  if (!w || !qs || !ds || !y) return Q4K_ERR_NULL;
+  if (m < 1 || m > Q4K_DECODE_MAX_TOKENS || k > kDecodeMaxK) return Q4K_ERR_SHAPE;
+  size_t wbytes;
+  int st = check_matrix(n, k, &wbytes);
+  if (st) return st;
+  if ((st = check_elems(m, k)) || (st = check_elems(m, n))) return st;
+  if (!aligned(w, kAlign) || !aligned(qs, kAlign) || !aligned(ds, 8) || !aligned(y, 4)) return Q4K_ERR_ALIGN;
+  if ((st = check_device())) return st;
+  return launch_status(launch_q8_gemv(static_cast<const uint8_t*>(w), qs, ds, y, m, n, k,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 int q4k_test_mmq_partials(const void* w, const int8_t* qs, int m, int n, int k,
                           int32_t* partials, void* stream) {
   if (!partials) return Q4K_ERR_NULL;

@@ -1,0 +1,228 @@
+// Q8_1-activation decode GEMV on the vector ALUs, gfx950.
+//
+// "realizar -- ffn.rs", fused_ffn_swiglu_gpu_true_dp4a: the activations are
+// quantised to Q8_1 (32 int8 values and one scale per block), each sub-block
+// product with the Q4_K quants is an integer dot product of packed bytes,
+// and the scales are applied afterwards.  For token t, weight row j and the
+// 32-value sub-block s:
+//   P = sum_{i<32} q_w * q_a                   (v_dot4_i32_i8, exact in int32)
+//   y[t][j] += (d*sc_s) * (d_a * P)  -  (dmin*m_s) * (d_a * S)
+// with S the integer block sum stored next to d_a.  This is the product
+// q4k_mmq computes, for the few tokens of a decode step, where a GEMM tile
+// would leave most of the matrix cores idle and the weight stream is what
+// costs.
+//
+// Activation-stationary layout.  A row is cut into 4*(k/256) slices of 64
+// weights (quarter g of a 256-block: quant bytes 32g..32g+31, whose low
+// nibbles are sub-block 2g and high nibbles sub-block 2g+1).  Each lane owns
+// one slice position for the whole kernel and holds the 64 activation quants
+// of that position for every token in registers (16 words per token), with
+// d_a and d_a*S of its two sub-blocks.  A wavefront covers 16 consecutive
+// blocks of a row; a row wider than that spans wr wavefronts, whose sums meet
+// in LDS.  Per row a lane loads 48 bytes (the 16-byte block header and its 32
+// quant bytes, raw buffer loads that read zeros past the last row); PF rows
+// are in flight per wavefront.  Lane sums are reduced across the row's lanes
+// in a fixed order (deterministic).  Tokens are processed MT at a time (1, 2,
+// 4 or 8); the missing ones read zeros and are not stored.
+#include "q4k_device.hpp"
+#include "q4k_internal.hpp"
+
+namespace q4k {
+
+namespace {
+
+constexpr int kQ8Threads = 512;
+constexpr int kQ8MaxRowsPerGroup = 64;
+
+struct Q8Geo {
+  int wr;    // wavefronts per row
+  int rs;    // row slots per workgroup (rows in flight side by side)
+  int rpg;   // rows per workgroup (a multiple of rs)
+};
+
+struct RowRaw {
+  uint4 h;   // block header
+  uint4 q0;  // quant bytes 32g .. 32g+15
+  uint4 q1;  // quant bytes 32g+16 .. 32g+31
+};
+
+__device__ __forceinline__ void load_row(rsrc_t r, uint32_t off, int g, RowRaw& raw) {
+  raw.h = buf_load16(r, off);
+  const uint32_t q = off == kOob ? kOob : off + 16u + 32u * static_cast<uint32_t>(g);
+  raw.q0 = buf_load16(r, q);
+  raw.q1 = buf_load16(r, q == kOob ? kOob : q + 16u);
+}
+
+// Sum over the 64 lanes (every lane gets the total).
+__device__ __forceinline__ float lane_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int MT, int PF>
+__global__ __launch_bounds__(kQ8Threads) void q8_gemv_kernel(const uint8_t* __restrict__ w,
+                                                             const int8_t* __restrict__ qs,
+                                                             const uint32_t* __restrict__ ds,
+                                                             float* __restrict__ y, int m, int n,
+                                                             int k, Q8Geo geo) {
+  extern __shared__ __attribute__((aligned(16))) float part[];  // [rpg][wr][MT]
+  const int K = k >> 8;
+  const int S = 4 * K;
+  const int nsub = k >> 5;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int slot = wave / geo.wr;  // uniform
+  const int wpart = wave - slot * geo.wr;
+  const int slice = wpart * 64 + lane;
+  const bool lane_ok = slice < S;
+  const int b = lane_ok ? slice >> 2 : 0;
+  const int g = slice & 3;
+
+  // 1. this lane's activations: token t, k = 256b + 64g .. +63 (sub-blocks
+  //    8b+2g and 8b+2g+1), read once
+  const rsrc_t rq = make_rsrc(qs, static_cast<uint32_t>(m) * static_cast<uint32_t>(k));
+  const rsrc_t rd = make_rsrc(ds, static_cast<uint32_t>(m) * static_cast<uint32_t>(nsub) * 4u);
+  uint32_t xa[MT][16];
+  float da0[MT], da1[MT], sa0[MT], sa1[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const uint32_t base = lane_ok ? static_cast<uint32_t>(t) * k + 256u * b + 64u * g : kOob;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 v = buf_load16(rq, base == kOob ? kOob : base + 16u * c);
+      xa[t][4 * c] = v.x;
+      xa[t][4 * c + 1] = v.y;
+      xa[t][4 * c + 2] = v.z;
+      xa[t][4 * c + 3] = v.w;
+    }
+    const uint32_t dofs = lane_ok ? (static_cast<uint32_t>(t) * nsub + 8u * b + 2u * g) * 4u : kOob;
+    const uint2 dw = buf_load8(rd, dofs);
+    da0[t] = half_bits_to_float(dw.x & 0xFFFFu);
+    da1[t] = half_bits_to_float(dw.y & 0xFFFFu);
+    sa0[t] = da0[t] * static_cast<float>(static_cast<int16_t>(dw.x >> 16));  // exact
+    sa1[t] = da1[t] * static_cast<float>(static_cast<int16_t>(dw.y >> 16));
+  }
+
+  // 2. the workgroup's rows: slot `slot` takes rows slot, slot + rs, ...
+  const int row0 = blockIdx.x * geo.rpg;
+  const int rows = min(geo.rpg, n - row0);
+  const size_t wofs = static_cast<size_t>(row0) * K * kBlockBytes;
+  const rsrc_t rw = make_rsrc(w + wofs, static_cast<uint32_t>(rows) * static_cast<uint32_t>(K) * kBlockBytes);
+  const uint32_t stride = static_cast<uint32_t>(geo.rs) * static_cast<uint32_t>(K) * kBlockBytes;
+  const uint32_t base = static_cast<uint32_t>(slot * K + b) * kBlockBytes;
+  const int nit = (rows - slot + geo.rs - 1) / geo.rs;  // rows of this slot (uniform)
+  auto row_off = [&](int it) -> uint32_t {
+    return lane_ok && it < nit ? base + static_cast<uint32_t>(it) * stride : kOob;
+  };
+  const int wgroups = (nit + PF - 1) / PF;
+
+  RowRaw raw[PF];
+#pragma unroll
+  for (int p = 0; p < PF; ++p) load_row(rw, row_off(p), g, raw[p]);
+
+  for (int grp = 0; grp < wgroups; ++grp) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int it = grp * PF + p;
+      // scales and quants of this lane's slice of the row
+      const uint4 h = raw[p].h;
+      const float d = half_bits_to_float(h.x & 0xFFFFu);
+      const float dmin = half_bits_to_float(h.x >> 16);
+      uint32_t sc0, mn0, sc1, mn1;
+      scale_min_rt(h, 2 * g, sc0, mn0);
+      scale_min_rt(h, 2 * g + 1, sc1, mn1);
+      const float ws0 = d * static_cast<float>(sc0), ws1 = d * static_cast<float>(sc1);  // exact
+      const float wm0 = dmin * static_cast<float>(mn0), wm1 = dmin * static_cast<float>(mn1);
+      const uint32_t qw[8] = {raw[p].q0.x, raw[p].q0.y, raw[p].q0.z, raw[p].q0.w,
+                              raw[p].q1.x, raw[p].q1.y, raw[p].q1.z, raw[p].q1.w};
+      // the next row of this register set is in flight while this one is used
+      load_row(rw, row_off(it + PF), g, raw[p]);
+      uint32_t lo[8], hi[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo[i] = qw[i] & 0x0F0F0F0Fu;          // sub-block 2g, weights 8i/2 ..: quant byte order
+        hi[i] = (qw[i] >> 4) & 0x0F0F0F0Fu;   // sub-block 2g+1
+      }
+      float acc[MT];
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        int p0 = 0, p1 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p0 = __builtin_amdgcn_sdot4(static_cast<int>(lo[i]), static_cast<int>(xa[t][i]), p0, false);
+          p1 = __builtin_amdgcn_sdot4(static_cast<int>(hi[i]), static_cast<int>(xa[t][8 + i]), p1, false);
+        }
+        float v = ws0 * (da0[t] * static_cast<float>(p0));
+        v = fmaf(ws1, da1[t] * static_cast<float>(p1), v);
+        v = fmaf(-wm0, sa0[t], v);
+        v = fmaf(-wm1, sa1[t], v);
+        acc[t] = lane_ok ? v : 0.f;
+      }
+      // row sums over the wavefront's lanes, then over the row's wavefronts
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[t] = lane_sum(acc[t]);
+      if (it < nit) {  // uniform
+        const int r = slot + it * geo.rs;
+        if (geo.wr == 1) {
+          if (lane < MT) {
+            float out = acc[0];
+#pragma unroll
+            for (int t = 1; t < MT; ++t) out = lane == t ? acc[t] : out;
+            if (lane < m) y[static_cast<size_t>(lane) * n + row0 + r] = out;
+          }
+        } else if (lane == 0) {
+#pragma unroll
+          for (int t = 0; t < MT; ++t) part[(r * geo.wr + wpart) * MT + t] = acc[t];
+        }
+      }
+    }
+  }
+  if (geo.wr > 1) {
+    __syncthreads();
+    for (int e = tid; e < rows * MT; e += blockDim.x) {
+      const int r = e / MT, t = e - r * MT;
+      float s = 0.f;
+      for (int q = 0; q < geo.wr; ++q) s += part[(r * geo.wr + q) * MT + t];
+      if (t < m) y[static_cast<size_t>(t) * n + row0 + r] = s;
+    }
+  }
+}
+
+Q8Geo make_q8_geo(int n, int k) {
+  Q8Geo g{};
+  const int S = 4 * (k / kQK);
+  g.wr = (S + 63) / 64;
+  g.rs = g.wr >= 4 ? 1 : (4 + g.wr - 1) / g.wr;
+  // about 256 workgroups (one per CU), at most 64 rows each, whole slots
+  long long want = (static_cast<long long>(n) + 255) / 256;
+  if (want < g.rs) want = g.rs;
+  if (want > kQ8MaxRowsPerGroup) want = kQ8MaxRowsPerGroup;
+  g.rpg = static_cast<int>((want + g.rs - 1) / g.rs * g.rs);
+  return g;
+}
+
+template <int MT>
+hipError_t launch_mt(const uint8_t* w, const int8_t* qs, const uint32_t* ds, float* y, int m, int n,
+                     int k, hipStream_t stream) {
+  constexpr int PF = MT >= 8 ? 2 : 4;
+  const Q8Geo g = make_q8_geo(n, k);
+  const size_t lds = g.wr > 1 ? static_cast<size_t>(g.rpg) * g.wr * MT * sizeof(float) : 0;
+  const dim3 grid((n + g.rpg - 1) / g.rpg);
+  q8_gemv_kernel<MT, PF><<<grid, dim3(64 * g.wr * g.rs), lds, stream>>>(w, qs, ds, y, m, n, k, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_q8_gemv(const uint8_t* w, const int8_t* qs, const uint32_t* ds, float* y, int m,
+                          int n, int k, hipStream_t stream) {
+  if (m < 1 || m > kMaxTokens || k < kQK || k % kQK || k > 32768 || n < 1) return hipErrorInvalidValue;
+  if (m == 1) return launch_mt<1>(w, qs, ds, y, m, n, k, stream);
+  if (m == 2) return launch_mt<2>(w, qs, ds, y, m, n, k, stream);
+  if (m <= 4) return launch_mt<4>(w, qs, ds, y, m, n, k, stream);
+  return launch_mt<8>(w, qs, ds, y, m, n, k, stream);
+}
+
+}  // namespace q4k

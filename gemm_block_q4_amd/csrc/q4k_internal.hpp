@@ -69,6 +69,11 @@ struct MmqArgs {
 
 hipError_t launch_mmq(const MmqArgs& a, hipStream_t stream);
 
+// Q8_1-activation decode GEMV: y [m][n] = reference dot of Q8_1 rows with the
+// Q4_K rows, 1 <= m <= 8, 256 <= k <= 32768 (validated by the caller).
+hipError_t launch_q8_gemv(const uint8_t* w, const int8_t* qs, const uint32_t* ds, float* y, int m,
+                          int n, int k, hipStream_t stream);
+
 // Number of k splits (1 .. max_splits) for the single-matrix MMQ pass of an
 // m x n x k product on a device with `cus` compute units: the one that
 // minimises the busiest compute unit's share of k blocks (a workgroup fills a

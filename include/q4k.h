@@ -131,6 +131,22 @@ int q8_1_quantize(const void* x, int x_dtype, int m, int k, int8_t* qs, uint32_t
 int q4k_mmq(const void* w, const int8_t* qs, const uint32_t* ds, float* y, int m, int n,
             int k, void* stream);
 
+/* Q8_1-activation decode GEMV ("ffn.rs", fused_ffn_swiglu_gpu_true_dp4a:
+   Q8_1 activations, integer dot products with the Q4_K quants, scales
+   applied afterwards): the q4k_mmq product for a decode step's few tokens,
+     P[t][j][b] = sum_{i<32} q_w[j][32b+i] * q_a[t][32b+i]      (int32, exact)
+     y[t][j] = sum_b (d*sc)[j][b] * d_a[t][b] * P - (dmin*m)[j][b] * d_a[t][b] * S[t][b]
+   with P from 4-byte integer dot products on the vector ALUs (each weight row
+   is read once for all m tokens).  w: device block_q4_K [n][k/256]; qs/ds:
+   device Q8_1 of the activations [m][k] (as written by q8_1_quantize); y:
+   device f32 [m][n], overwritten.  1 <= m <= 8, n >= 1, 256 <= k <= 32768,
+   k % 256 == 0.  Scales are applied in f32; the result agrees with q4k_mmq
+   to f32 rounding.
+   Errors: Q4K_ERR_NULL, Q4K_ERR_SHAPE, Q4K_ERR_ALIGN, Q4K_ERR_OVERFLOW,
+   Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */
+int q4k_q8_gemv(const void* w, const int8_t* qs, const uint32_t* ds, float* y, int m, int n,
+                int k, void* stream);
+
 /* Test hook on the same device code as q4k_mmq: writes the integer partials
    partials[t][j][b] = P[t][j][b] (int32 [m][n][k/32], device) instead of y.
    Same shape rules as q4k_mmq; meant for small shapes. */

@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert {"q4k_gemv", "q8_1_quantize", "q4k_mmq", "ffn_swiglu_q4k", "q4k_weight_bytes",
             "q4k_status_string", "ffn_swiglu_q4k_workspace_bytes",
-            "q4k_test_mmq_partials"} <= set(names)
+            "q4k_test_mmq_partials", "q4k_q8_gemv"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -76,6 +76,16 @@ def test_mmq_validation(lib):
     assert lib.q4k_mmq(P, P + 1, P, P, 1, 1, 256, None) == 3
     assert lib.q4k_test_mmq_partials(P, P, 1, 1, 256, None, None) == 1
     assert lib.q4k_mmq(P, P, P, P, 1, 1, (1 << 20) + 256, None) == 2  # k above the prefill limit
+
+
+def test_q8_gemv_validation(lib):
+    assert lib.q4k_q8_gemv(P, P, None, P, 1, 1, 256, None) == 1
+    assert lib.q4k_q8_gemv(P, P, P, P, 0, 1, 256, None) == 2
+    assert lib.q4k_q8_gemv(P, P, P, P, 9, 1, 256, None) == 2          # more than 8 tokens
+    assert lib.q4k_q8_gemv(P, P, P, P, 1, 1, 512 + 32, None) == 2     # k not a multiple of 256
+    assert lib.q4k_q8_gemv(P, P, P, P, 1, 1, 32768 + 256, None) == 2  # k above the decode limit
+    assert lib.q4k_q8_gemv(P, P + 4, P, P, 1, 1, 256, None) == 3      # misaligned quants
+    assert lib.q4k_q8_gemv(P, P, P + 4, P, 1, 1, 256, None) == 3      # misaligned scale words
 
 
 def test_ffn_validation(lib):
