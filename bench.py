@@ -11,7 +11,8 @@ that host launch overhead is not measured.
 
 Also reported (``secondary``): the 7B-style decode FFN at 1/4/8 tokens, the
 prefill FFN (Q8_1 + MMQ) at 512 and 2048 tokens in TOPS, the 64-expert top-8
-MoE decode FFN, and the roofline of the dominant kernel.  ``cpu_baseline``
+MoE decode FFN, the Q8_1-activation GEMV (q4k_q8_gemv) on the sweep shapes at
+1/4/8 tokens, and the roofline of the dominant kernel.  ``cpu_baseline``
 times the CPU oracle on a bounded sample of the headline workload.
 """
 
@@ -193,6 +194,34 @@ def decode_ffn(q4k, synth, reps=40):
     return out
 
 
+def q8_gemv(q4k, synth):
+    """Q8_1-activation decode GEMV (q4k_q8_gemv) on the sweep shapes at 1, 4 and
+    8 tokens: average launch time over a graph of launches on rotated weight
+    copies, and effective weight-GB/s.  The activations are quantised once by
+    q8_1_quantize before timing."""
+    import torch
+    out = {}
+    for s, (n, k) in enumerate(synth.GEMV_SWEEP_SHAPES):
+        _, _, w, _ = synth.gemv_sweep_case(s)
+        copies = rotated(w)
+        nbytes = q4k.q4k_weight_bytes(n, k)
+        for m in (1, 4, 8):
+            x = torch.from_numpy(synth.activations(synth.GEMV_SWEEP, m, k, True, sub=100 + m)).cuda()
+            qs = torch.empty((m, k), dtype=torch.int8, device="cuda")
+            ds = torch.empty((m, k // 32), dtype=torch.int32, device="cuda")
+            q4k.q8_1_quantize(x, q4k.Q4K_F32, m, k, qs, ds)
+            y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+
+            def call(i, copies=copies, qs=qs, ds=ds, y=y, m=m, n=n, k=k):
+                q4k.q4k_q8_gemv(copies[i % len(copies)], qs, ds, y, m, n, k)
+
+            reps = len(copies)
+            ms = timed_graph(call, reps, reps)
+            us = ms * 1e3 / reps
+            out[f"n{n}_k{k}_m{m}"] = dict(us=round(us, 2), weight_gbs=round(nbytes / (us * 1e-6) / 1e9, 1))
+    return out
+
+
 def prefill_ffn(q4k, synth, reps=4):
     import torch
     hidden, inter = 5120, 17408
@@ -321,6 +350,8 @@ def main():
         secondary["prefill_ffn_5120_17408"] = prefill_ffn(q4k, synth)
         log("bench: MoE")
         secondary["moe_64x_top8_2048_768"] = moe_ffn(q4k, synth)
+        log("bench: Q8_1-activation GEMV")
+        secondary["q8_gemv_sweep"] = q8_gemv(q4k, synth)
 
     cpu = None
     if not args.skip_cpu:

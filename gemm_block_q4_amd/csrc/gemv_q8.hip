@@ -22,8 +22,8 @@
 // in LDS.  Per row a lane loads 48 bytes (the 16-byte block header and its 32
 // quant bytes, raw buffer loads that read zeros past the last row); PF rows
 // are in flight per wavefront.  Lane sums are reduced across the row's lanes
-// in a fixed order (deterministic).  Tokens are processed MT at a time (1, 2,
-// 4 or 8); the missing ones read zeros and are not stored.
+// with DPP in a fixed order (deterministic).  Tokens are processed MT at a
+// time (1, 2, 4 or 8); the missing ones read zeros and are not stored.
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
 
@@ -53,10 +53,23 @@ __device__ __forceinline__ void load_row(rsrc_t r, uint32_t off, int g, RowRaw& 
   raw.q1 = buf_load16(r, q == kOob ? kOob : q + 16u);
 }
 
-// Sum over the 64 lanes (every lane gets the total).
-__device__ __forceinline__ float lane_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+// Lane permute on the VALU (DPP; no LDS round trip).  Lanes whose source is
+// out of range read 0.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               ROW_MASK, 0xF, true));
+}
+
+// Sum over the 64 lanes, landing in lane 63: within quads, then rows of 16
+// (row_shr 4, 8), then across rows (row_bcast 15 and 31).
+__device__ __forceinline__ float wave_total_last(float v) {
+  v += dpp_f<0xB1>(v);        // quad_perm(1,0,3,2)
+  v += dpp_f<0x4E>(v);        // quad_perm(2,3,0,1)
+  v += dpp_f<0x114>(v);       // row_shr:4
+  v += dpp_f<0x118>(v);       // row_shr:8
+  v += dpp_f<0x142, 0xA>(v);  // row_bcast:15 into rows 1, 3
+  v += dpp_f<0x143, 0xC>(v);  // row_bcast:31 into rows 2, 3
   return v;
 }
 
@@ -142,8 +155,8 @@ __global__ __launch_bounds__(kQ8Threads) void q8_gemv_kernel(const uint8_t* __re
       uint32_t lo[8], hi[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        lo[i] = qw[i] & 0x0F0F0F0Fu;          // sub-block 2g, weights 8i/2 ..: quant byte order
-        hi[i] = (qw[i] >> 4) & 0x0F0F0F0Fu;   // sub-block 2g+1
+        lo[i] = qw[i] & 0x0F0F0F0Fu;         // sub-block 2g, positions 4i .. 4i+3
+        hi[i] = (qw[i] >> 4) & 0x0F0F0F0Fu;  // sub-block 2g+1, same positions
       }
       float acc[MT];
 #pragma unroll
@@ -160,19 +173,17 @@ __global__ __launch_bounds__(kQ8Threads) void q8_gemv_kernel(const uint8_t* __re
         v = fmaf(-wm1, sa1[t], v);
         acc[t] = lane_ok ? v : 0.f;
       }
-      // row sums over the wavefront's lanes, then over the row's wavefronts
+      // row sums over the wavefront's lanes (in lane 63), then over the
+      // row's wavefronts
 #pragma unroll
-      for (int t = 0; t < MT; ++t) acc[t] = lane_sum(acc[t]);
-      if (it < nit) {  // uniform
+      for (int t = 0; t < MT; ++t) acc[t] = wave_total_last(acc[t]);
+      if (it < nit && lane == 63) {
         const int r = slot + it * geo.rs;
         if (geo.wr == 1) {
-          if (lane < MT) {
-            float out = acc[0];
 #pragma unroll
-            for (int t = 1; t < MT; ++t) out = lane == t ? acc[t] : out;
-            if (lane < m) y[static_cast<size_t>(lane) * n + row0 + r] = out;
-          }
-        } else if (lane == 0) {
+          for (int t = 0; t < MT; ++t)
+            if (t < m) y[static_cast<size_t>(t) * n + row0 + r] = acc[t];
+        } else {
 #pragma unroll
           for (int t = 0; t < MT; ++t) part[(r * geo.wr + wpart) * MT + t] = acc[t];
         }
