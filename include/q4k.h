@@ -140,8 +140,9 @@ int q4k_mmq(const void* w, const int8_t* qs, const uint32_t* ds, float* y, int m
    is read once for all m tokens).  w: device block_q4_K [n][k/256]; qs/ds:
    device Q8_1 of the activations [m][k] (as written by q8_1_quantize); y:
    device f32 [m][n], overwritten.  1 <= m <= 8, n >= 1, 256 <= k <= 32768,
-   k % 256 == 0.  Scales are applied in f32; the result agrees with q4k_mmq
-   to f32 rounding.
+   k % 256 == 0; ds must be 8-byte aligned (each lane reads the words of two
+   sub-blocks at once).  Scales are applied in f32; the result agrees with
+   q4k_mmq to f32 rounding.
    Errors: Q4K_ERR_NULL, Q4K_ERR_SHAPE, Q4K_ERR_ALIGN, Q4K_ERR_OVERFLOW,
    Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */
 int q4k_q8_gemv(const void* w, const int8_t* qs, const uint32_t* ds, float* y, int m, int n,

@@ -62,6 +62,16 @@ def test_q8_gemv_integer_special_case_bit_exact(lib):
     assert np.array_equal(y.astype(np.float64), (qa.astype(np.int64) @ qw.T).astype(np.float64))
 
 
+@pytest.mark.parametrize("m,n,k", [(3, 13000, 256), (7, 20000, 512), (2, 300, 16384)])
+def test_q8_gemv_many_workgroups(lib, m, n, k):
+    # rows per workgroup at their cap of 64 (many workgroups, a ragged last
+    # one), and rows spanning four wavefronts
+    say(f"q8 gemv m={m} n={n} k={k}")
+    w = synth.random_q4k(synth.rng(94, 1, n + k), n, k)
+    qs, d16, s = quantised(m, k, 5)
+    check(lib, w, qs, d16, s, n, k)
+
+
 @pytest.mark.parametrize("m,n,k", [(8, 11008, 4096), (4, 4096, 11008)])
 def test_q8_gemv_decode_shapes(lib, m, n, k):
     # the 7B-style decode projections, checked against the oracle and against
