@@ -116,18 +116,6 @@ __device__ __forceinline__ float dpp(float v) {
                                                                ROW_MASK, 0xF, true));
 }
 
-// Maximum of non-negative values over the wavefront, in every lane (lanes
-// outside a DPP row read 0, the identity here).
-__device__ __forceinline__ float wave_max_nonneg(float v) {
-  v = fmaxf(v, dpp<0xB1>(v));        // quad_perm(1,0,3,2)
-  v = fmaxf(v, dpp<0x4E>(v));        // quad_perm(2,3,0,1)
-  v = fmaxf(v, dpp<0x114>(v));       // row_shr:4
-  v = fmaxf(v, dpp<0x118>(v));       // row_shr:8
-  v = fmaxf(v, dpp<0x142, 0xA>(v));  // row_bcast:15
-  v = fmaxf(v, dpp<0x143, 0xC>(v));  // row_bcast:31
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-
 // Exponent that maps a maximum |x| into [2^14, 2^15) (0 when all values are
 // zero).
 __device__ __forceinline__ int block_shift(float amax) {
@@ -154,25 +142,94 @@ __device__ __forceinline__ float hi_half(uint32_t v) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v >> 16)));
 }
 
+// Per-token maxima of non-negative values over the wavefront (MT = 4 or 8).
+// Lane swaps between half-waves and between rows (permlane32/16) take the
+// maximum of token pairs and halve the number of values per step; DPP max
+// steps finish within rows.  Each token's maximum ends in one lane, which
+// max_lanes finds once per kernel.
+__device__ __forceinline__ float swap_max32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_max16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+template <int MT>
+__device__ __forceinline__ float token_max(const float (&am)[MT], int lane) {
+  static_assert(MT == 4 || MT == 8, "token count");
+  float w[MT / 2];
+#pragma unroll
+  for (int j = 0; j < MT / 2; ++j) w[j] = swap_max32(am[2 * j], am[2 * j + 1]);
+  float x[MT / 4];
+#pragma unroll
+  for (int i = 0; i < MT / 4; ++i) x[i] = swap_max16(w[2 * i], w[2 * i + 1]);
+  float y;
+  if constexpr (MT == 4) {
+    y = fmaxf(x[0], dpp<0x128>(x[0]));  // row_ror:8 (lane xor 8 within a row)
+  } else {
+    const bool b3 = (lane >> 3) & 1;    // lanes 8..15 of a row keep x1, 0..7 x0
+    y = fmaxf(b3 ? x[1] : x[0], dpp<0x128>(b3 ? x[0] : x[1]));
+  }
+  y = fmaxf(y, dpp<0xB1>(y));   // quad_perm(1,0,3,2)
+  y = fmaxf(y, dpp<0x4E>(y));   // quad_perm(2,3,0,1)
+  y = fmaxf(y, dpp<0x114>(y));  // row_shr:4: lanes 4..7 of each half-row hold the result
+  return y;
+}
+
+// Lane holding token t's maximum after token_max (uniform), found by running
+// the same swaps on token indices.
+template <int MT>
+__device__ __forceinline__ void max_lanes(int lane, int (&tl)[MT]) {
+  uint32_t w[MT / 2];
+#pragma unroll
+  for (int j = 0; j < MT / 2; ++j) w[j] = __builtin_amdgcn_permlane32_swap(2u * j, 2u * j + 1u, false, false)[0];
+  uint32_t x[MT / 4];
+#pragma unroll
+  for (int i = 0; i < MT / 4; ++i) x[i] = __builtin_amdgcn_permlane16_swap(w[2 * i], w[2 * i + 1], false, false)[0];
+  int tok;
+  bool holder;
+  if constexpr (MT == 4) {
+    tok = static_cast<int>(x[0]);
+    holder = (lane & 15) == 15;
+  } else {
+    tok = static_cast<int>((lane >> 3) & 1 ? x[1] : x[0]);
+    holder = (lane & 7) == 7;
+  }
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const unsigned long long m = __ballot(holder && tok == t);
+    tl[t] = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(m)));
+  }
+}
+
 template <int MT, typename XT>
 __device__ __forceinline__ void convert_chunk(WaveLds<MT>& L, const XT (&xv)[MT][WaveLds<MT>::kCH],
-                                              int mt, int nb, int lane) {
+                                              int mt, int nb, int lane, const int (&tl)[MT]) {
   constexpr int CH = WaveLds<MT>::kCH;
   constexpr int R2 = WaveLds<MT>::kR2;
   constexpr int HR = R2 / 2;
   const int s = (lane & 15) >> 1;
   const int g = lane >> 4;
   const int half = lane & 1;
+  // every token's maximum at once (tokens past `mt` were loaded as zeros)
+  float am[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    float v = 0.f;
+#pragma unroll
+    for (int bi = 0; bi < CH; ++bi) {
+      const float4 x = widen(xv[t][bi]);
+      v = fmaxf(v, fmaxf(fmaxf(fabsf(x.x), fabsf(x.y)), fmaxf(fabsf(x.z), fabsf(x.w))));
+    }
+    am[t] = v;
+  }
+  const float tmax = token_max<MT>(am, lane);
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     if (t >= mt) break;
-    float amax = 0.f;
-#pragma unroll
-    for (int bi = 0; bi < CH; ++bi) {
-      const float4 v = widen(xv[t][bi]);
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
-    }
-    amax = wave_max_nonneg(amax);
+    const float amax = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, tmax), tl[t]));
     const int sh = block_shift(amax);
 #pragma unroll
     for (int bi = 0; bi < CH; ++bi) {
@@ -279,6 +336,8 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(GemvArgs a) {
   const int K = a.k / kQK;
 
   const int mt = min(a.m, MT);  // live tokens (rows of x and y)
+  int tl[MT];                   // lane of each token's maximum in token_max
+  max_lanes<MT>(lane, tl);
 
   // this workgroup's RT tiles of 16 rows
   const int n0 = blockIdx.x * (RT * kRows);
@@ -346,7 +405,7 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(GemvArgs a) {
   auto chunk = [&](auto hn) {
     constexpr bool HN = decltype(hn)::value;
     // 1. activations -> operand layout in this wavefront's LDS
-    convert_chunk<MT, XT>(L, xv, mt, nb, lane);
+    convert_chunk<MT, XT>(L, xv, mt, nb, lane, tl);
     lds_fence();
     const int cn = cb + CH;
     const int nbn = HN ? min(CH, kb1 - cn) : 0;
