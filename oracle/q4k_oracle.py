@@ -195,6 +195,77 @@ def gemv(w: np.ndarray, rows: int, cols: int, x: np.ndarray) -> np.ndarray:
 
 # -- Q8_1 activation quantisation --------------------------------------------
 
+def pack_quants(q: np.ndarray) -> np.ndarray:
+    """Inverse of :func:`unpack_quants` (256 quants 0..15 -> 128 bytes)."""
+    q = np.asarray(q, dtype=np.uint8)
+    if q.max(initial=0) > 15:
+        raise ValueError("quants are 4-bit")
+    out = np.empty(q.shape[:-1] + (128,), dtype=np.uint8)
+    for g in range(4):
+        out[..., 32 * g: 32 * g + 32] = q[..., 64 * g: 64 * g + 32] | (q[..., 64 * g + 32: 64 * g + 64] << 4)
+    return out
+
+
+def _f16_saturating(v: np.ndarray) -> np.ndarray:
+    """binary32 -> binary16 (nearest even), 65504 where the rounding would overflow."""
+    v = np.asarray(v, dtype=np.float32)
+    return np.where(v >= F16_OVERFLOW, np.float32(F16_MAX), v).astype(np.float16)
+
+
+def q4k_quantize(x: np.ndarray) -> np.ndarray:
+    """block_q4_K encoding of weights [rows, cols], cols a multiple of 256.
+
+    "q4k_mmq.rs", ``quantize_weight_q4k``, names a load-time quantiser to the
+    GGML block_q4_K format but prints no algorithm.  Reading taken (the
+    plainest fit of the format, not GGML's scale search), every step in
+    binary32 with round-to-nearest-even, per 32-value sub-block j of a
+    256-value block:
+
+    * ``lo_j = min(0, min w)``, ``hi_j = max w``; the offset ``o_j = 0 - lo_j``
+      (+0, not -0, when nothing is negative) and the step
+      ``s_j = (hi_j - lo_j) / 15`` map the sub-block onto 0..15;
+    * ``d = binary16(max_j s_j / 63)``, ``dmin = binary16(max_j o_j / 63)``
+      (saturating at 65504 as for Q8_1);
+    * ``sc_j = rint(s_j / d)`` and ``m_j = rint(o_j / dmin)``, clamped to
+      0..63 (0 when the divisor is 0);
+    * ``q = rint((w + dmin*m_j) / (d*sc_j))`` clamped to 0..15 (0 when
+      ``d*sc_j`` is 0), so ``d*sc_j*q - dmin*m_j`` is the nearest value on
+      the block's grid.
+
+    bf16 input is widened to f32 exactly by the caller.  Returns uint8
+    [rows * cols/256 * 144].  Input must be finite.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    if x.ndim != 2 or x.shape[1] % QK_K:
+        raise ValueError("x must be [rows, cols] with cols a multiple of 256")
+    if not np.all(np.isfinite(x)):
+        raise ValueError("Q4_K input must be finite")
+    rows, cols = x.shape
+    nb = cols // QK_K
+    xb = x.reshape(rows, nb, 8, SUB_BLOCK)
+    lo = np.minimum(xb.min(axis=-1), np.float32(0.0))
+    hi = xb.max(axis=-1)
+    o = (np.float32(0.0) - lo).astype(np.float32)  # +0 when nothing is negative
+    s = ((hi - lo).astype(np.float32) / np.float32(15.0)).astype(np.float32)
+    d16 = _f16_saturating(s.max(axis=-1) / np.float32(63.0))
+    m16 = _f16_saturating(o.max(axis=-1) / np.float32(63.0))
+    d = d16.astype(np.float32)[..., None]
+    dmin = m16.astype(np.float32)[..., None]
+    sc = np.where(d > 0, np.clip(np.rint(s / np.where(d > 0, d, np.float32(1.0))), 0, 63), 0).astype(np.int64)
+    mn = np.where(dmin > 0, np.clip(np.rint(o / np.where(dmin > 0, dmin, np.float32(1.0))), 0, 63), 0).astype(np.int64)
+    ds = (d * sc.astype(np.float32)).astype(np.float32)          # exact: 11 x 6 bits
+    dm = (dmin * mn.astype(np.float32)).astype(np.float32)
+    num = (xb + dm[..., None]).astype(np.float32)
+    ratio = (num / np.where(ds > 0, ds, np.float32(1.0))[..., None]).astype(np.float32)
+    q = np.where(ds[..., None] > 0, np.clip(np.rint(ratio), 0, 15), 0).astype(np.uint8)
+    out = np.empty((rows, nb, Q4K_BLOCK_BYTES), dtype=np.uint8)
+    out[..., 0:2] = d16.view(np.uint8).reshape(rows, nb, 2)
+    out[..., 2:4] = m16.view(np.uint8).reshape(rows, nb, 2)
+    out[..., 4:16] = pack_scale_min(sc, mn)
+    out[..., 16:] = pack_quants(q.reshape(rows, nb, QK_K))
+    return out.reshape(-1)
+
+
 def q8_1_quantize(x: np.ndarray):
     """Q8_1 encoding of f32 activations [m, k], k a multiple of 32.
 
