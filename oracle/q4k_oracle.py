@@ -223,7 +223,8 @@ def q4k_quantize(x: np.ndarray) -> np.ndarray:
 
     * ``lo_j = min(0, min w)``, ``hi_j = max w``; the offset ``o_j = 0 - lo_j``
       (+0, not -0, when nothing is negative) and the step
-      ``s_j = (hi_j - lo_j) / 15`` map the sub-block onto 0..15;
+      ``s_j = (hi_j - lo_j) / 15`` (+0 when ``hi_j == lo_j``, so that zeros
+      of either sign give the same bytes) map the sub-block onto 0..15;
     * ``d = binary16(max_j s_j / 63)``, ``dmin = binary16(max_j o_j / 63)``
       (saturating at 65504 as for Q8_1);
     * ``sc_j = rint(s_j / d)`` and ``m_j = rint(o_j / dmin)``, clamped to
@@ -246,7 +247,7 @@ def q4k_quantize(x: np.ndarray) -> np.ndarray:
     lo = np.minimum(xb.min(axis=-1), np.float32(0.0))
     hi = xb.max(axis=-1)
     o = (np.float32(0.0) - lo).astype(np.float32)  # +0 when nothing is negative
-    s = ((hi - lo).astype(np.float32) / np.float32(15.0)).astype(np.float32)
+    s = np.where(hi > lo, (hi - lo).astype(np.float32) / np.float32(15.0), np.float32(0.0)).astype(np.float32)
     d16 = _f16_saturating(s.max(axis=-1) / np.float32(63.0))
     m16 = _f16_saturating(o.max(axis=-1) / np.float32(63.0))
     d = d16.astype(np.float32)[..., None]
