@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     q4k_gemv,
     q4k_mmq,
     q4k_q8_gemv,
+    q4k_quantize,
     q4k_test_mmq_partials,
     q4k_weight_bytes,
     q8_1_quantize,

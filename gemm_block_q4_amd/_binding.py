@@ -39,6 +39,7 @@ _SIGNATURES = {
     "q4k_mmq": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _VP]),
     "q4k_test_mmq_partials": (_I, [_VP, _VP, _I, _I, _I, _VP, _VP]),
     "q4k_q8_gemv": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _VP]),
+    "q4k_quantize": (_I, [_VP, _I, _I, _I, _VP, _VP]),
     "ffn_swiglu_q4k_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "ffn_swiglu_q4k": (_I, [_VP, _VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP, _I, _I, _VP,
                             _VP, _SZ, _VP]),
@@ -112,6 +113,11 @@ def q8_1_quantize(x, x_dtype: int, m: int, k: int, qs, ds, stream=None) -> None:
 def q4k_mmq(w, qs, ds, y, m: int, n: int, k: int, stream=None) -> None:
     _check(load_library().q4k_mmq(_ptr(w), _ptr(qs), _ptr(ds), _ptr(y), m, n, k,
                                   _stream(stream)))
+
+
+def q4k_quantize(x, x_dtype: int, rows: int, cols: int, w, stream=None) -> None:
+    """Encode weights x [rows, cols] (f32 or bf16 bits) to block_q4_K bytes w."""
+    _check(load_library().q4k_quantize(_ptr(x), x_dtype, rows, cols, _ptr(w), _stream(stream)))
 
 
 def q4k_q8_gemv(w, qs, ds, y, m: int, n: int, k: int, stream=None) -> None:

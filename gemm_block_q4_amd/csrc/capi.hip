@@ -201,6 +201,20 @@ int q8_1_quantize(const void* x, int x_dtype, int m, int k, int8_t* qs, uint32_t
                                             static_cast<hipStream_t>(stream)));
 }
 
+int q4k_quantize(const void* x, int x_dtype, int rows, int cols, void* w, void* stream) {
+  if (!x || !w) return Q4K_ERR_NULL;
+  if (x_dtype != Q4K_F32 && x_dtype != Q4K_BF16) return Q4K_ERR_SHAPE;
+  if (rows < 1 || cols < Q4K_QK) return Q4K_ERR_SHAPE;
+  size_t wbytes;
+  int st = check_matrix(rows, cols, &wbytes);
+  if (st) return st;
+  if ((st = check_elems(rows, cols))) return st;
+  if (!aligned(x, x_dtype == Q4K_F32 ? 16 : 8) || !aligned(w, kAlign)) return Q4K_ERR_ALIGN;
+  if ((st = check_device())) return st;
+  return launch_status(launch_quantize_q4k(x, x_dtype == Q4K_BF16, rows, cols, static_cast<uint8_t*>(w),
+                                           static_cast<hipStream_t>(stream)));
+}
+
 static int mmq_common(const void* w, const int8_t* qs, const uint32_t* ds, float* y,
                       int32_t* partials, int m, int n, int k, void* stream) {
   if (!w || !qs || (!partials && (!ds || !y))) return Q4K_ERR_NULL;

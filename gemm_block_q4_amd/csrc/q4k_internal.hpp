@@ -44,6 +44,10 @@ hipError_t launch_gemv_mfma(const GemvArgs& a, hipStream_t stream);
 // fit one wavefront (k <= 4096); hipErrorNotSupported otherwise.
 hipError_t launch_moe_down(const GemvArgs& a, hipStream_t stream);
 
+// Load-time Q4_K quantiser: x [rows][cols] (f32 or bf16) -> block_q4_K.
+hipError_t launch_quantize_q4k(const void* x, int x_bf16, int rows, int cols, uint8_t* w,
+                               hipStream_t stream);
+
 hipError_t launch_q8_1_quantize(const void* x, int x_bf16, int m, int k, int8_t* qs,
                                 uint32_t* ds, hipStream_t stream);
 

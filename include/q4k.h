@@ -106,6 +106,25 @@ const char* q4k_status_string(int status);
    Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */
 int q4k_gemv(const void* w, const float* x, float* y, int m, int n, int k, void* stream);
 
+/* Load-time Q4_K weight quantiser ("q4k_mmq.rs", quantize_weight_q4k:
+   weights are encoded to GGML block_q4_K at load time; the pages print no
+   algorithm).  The plain min/max fit, every step in binary32 with
+   round-to-nearest-even, for each 32-value sub-block j of a 256-value block:
+     lo = min(0, min x), hi = max x, o = 0 - lo, s = hi > lo ? (hi - lo)/15 : 0
+     d = binary16(max_j s / 63), dmin = binary16(max_j o / 63)  (65504 where
+     the rounding would overflow)
+     sc_j = rint(s_j / d), m_j = rint(o_j / dmin), clamped to 0..63 (0 when
+     the divisor is 0)
+     q = rint((x + dmin*m_j) / (d*sc_j)), clamped to 0..15 (0 when d*sc_j = 0)
+   Bit-exact by construction (IEEE operations only).  x: device [rows][cols]
+   of x_dtype (Q4K_F32, or Q4K_BF16 widened exactly); w: device block_q4_K
+   [rows][cols/256] (q4k_weight_bytes(rows, cols) bytes), overwritten.
+   rows >= 1, cols >= 256, cols % 256 == 0.  Inputs must be finite
+   (non-finite input gives undefined codes but never faults).
+   Errors: Q4K_ERR_NULL, Q4K_ERR_SHAPE, Q4K_ERR_ALIGN, Q4K_ERR_OVERFLOW,
+   Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */
+int q4k_quantize(const void* x, int x_dtype, int rows, int cols, void* w, void* stream);
+
 /* Q8_1 activation quantisation ("q4k_mmq.rs", quantize_act_q8_1; "ffn.rs",
    q8_quantize_async): for each row t and 32-value block b of x,
      amax = max |x|, d = amax / 127 (binary32), q = rint(x / d) (binary32

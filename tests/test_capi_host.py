@@ -34,7 +34,7 @@ def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert {"q4k_gemv", "q8_1_quantize", "q4k_mmq", "ffn_swiglu_q4k", "q4k_weight_bytes",
             "q4k_status_string", "ffn_swiglu_q4k_workspace_bytes",
-            "q4k_test_mmq_partials", "q4k_q8_gemv"} <= set(names)
+            "q4k_test_mmq_partials", "q4k_q8_gemv", "q4k_quantize"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -86,6 +86,17 @@ def test_q8_gemv_validation(lib):
     assert lib.q4k_q8_gemv(P, P, P, P, 1, 1, 32768 + 256, None) == 2  # k above the decode limit
     assert lib.q4k_q8_gemv(P, P + 4, P, P, 1, 1, 256, None) == 3      # misaligned quants
     assert lib.q4k_q8_gemv(P, P, P + 4, P, 1, 1, 256, None) == 3      # misaligned scale words
+
+
+def test_quantize_validation(lib):
+    assert lib.q4k_quantize(None, 0, 1, 256, P, None) == 1
+    assert lib.q4k_quantize(P, 0, 1, 256, None, None) == 1
+    assert lib.q4k_quantize(P, 7, 1, 256, P, None) == 2          # unknown dtype
+    assert lib.q4k_quantize(P, 0, 0, 256, P, None) == 2
+    assert lib.q4k_quantize(P, 0, 1, 300, P, None) == 2          # cols not a multiple of 256
+    assert lib.q4k_quantize(P + 4, 0, 1, 256, P, None) == 3      # f32 input needs 16 bytes
+    assert lib.q4k_quantize(P + 8, 1, 1, 256, P + 4, None) == 3  # misaligned output
+    assert lib.q4k_quantize(P, 0, 1 << 30, 32768, P, None) == 4  # block count overflows
 
 
 def test_ffn_validation(lib):
