@@ -12,7 +12,8 @@ that host launch overhead is not measured.
 Also reported (``secondary``): the 7B-style decode FFN at 1/4/8 tokens, the
 prefill FFN (Q8_1 + MMQ) at 512 and 2048 tokens in TOPS, the 64-expert top-8
 MoE decode FFN, the Q8_1-activation GEMV (q4k_q8_gemv) on the sweep shapes at
-1/4/8 tokens, and the roofline of the dominant kernel.  ``cpu_baseline``
+1/4/8 tokens, the load-time Q4_K quantiser, and the roofline of the dominant
+kernel.  ``cpu_baseline``
 times the CPU oracle on a bounded sample of the headline workload.
 """
 
@@ -222,6 +223,31 @@ def q8_gemv(q4k, synth):
     return out
 
 
+def quantize_q4k(q4k, synth):
+    """Load-time Q4_K quantiser (q4k_quantize) on the [11008, 4096] matrix from
+    f32 and from bf16: average launch time over a graph of launches on rotated
+    input copies (>= 1 GiB), and GB/s of input plus output bytes."""
+    import torch
+    rows, cols = 11008, 4096
+    x = synth.activations(synth.GEMV_SWEEP, rows, cols, False, sub=200)
+    out_bytes = q4k.q4k_weight_bytes(rows, cols)
+    w = torch.empty(out_bytes, dtype=torch.uint8, device="cuda")
+    res = {}
+    for name, arr, dt in (("f32", x, q4k.Q4K_F32), ("bf16", synth.to_bf16_bits(x), q4k.Q4K_BF16)):
+        raw = rotated(arr.view(np.uint8).reshape(-1))
+        src = [c.view(torch.float32 if dt == q4k.Q4K_F32 else torch.int16) for c in raw]
+
+        def call(i, src=src, dt=dt):
+            q4k.q4k_quantize(src[i % len(src)], dt, rows, cols, w)
+
+        reps = len(src)
+        ms = timed_graph(call, reps, reps)
+        us = ms * 1e3 / reps
+        moved = arr.nbytes + out_bytes
+        res[name] = dict(us=round(us, 2), gbs=round(moved / (us * 1e-6) / 1e9, 1))
+    return res
+
+
 def prefill_ffn(q4k, synth, reps=4):
     import torch
     hidden, inter = 5120, 17408
@@ -352,6 +378,8 @@ def main():
         secondary["moe_64x_top8_2048_768"] = moe_ffn(q4k, synth)
         log("bench: Q8_1-activation GEMV")
         secondary["q8_gemv_sweep"] = q8_gemv(q4k, synth)
+        log("bench: Q4_K quantiser")
+        secondary["q4k_quantize_11008_4096"] = quantize_q4k(q4k, synth)
 
     cpu = None
     if not args.skip_cpu:
