@@ -13,8 +13,9 @@
 // rounded divide, rint, exact products), so the bytes are reproducible.
 //
 // One wavefront per block: lane l holds values 4l .. 4l+3 (sub-block l/8).
-// Sub-block extrema take three lane exchanges among its 8 lanes and the
-// block maxima three more; lane l < 8 of each 16 packs its four quants with
+// Sub-block extrema take three register-level lane exchanges among its 8 lanes
+// (DPP) and the block maxima three more (DPP and the gfx950 row/half swaps), so
+// no exchange goes through the LDS; lane l < 8 of each 16 packs its four quants with
 // the four of lane l+8 (the high nibbles, sub-block 2g+1) into one word of
 // the quant field, and lane 0 writes the header.  The kernel is bound by the
 // bytes it reads (4 or 2 per value) and writes (0.5625 per value).
@@ -27,6 +28,33 @@ namespace {
 
 constexpr int kQzThreads = 256;  // four blocks per workgroup, one per wavefront
 
+// DPP move of v (row_mask all rows); lanes outside BANKS (4-lane groups of a
+// 16-lane row) keep old
+template <int CTRL, int BANKS>
+__device__ __forceinline__ float dpp_move(float old, float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, v), CTRL, 0xF,
+                                                               BANKS, false));
+}
+
+// v of lane ^ 1, ^ 2, ^ 4 and ^ 8
+__device__ __forceinline__ float lane_xor1(float v) { return dpp_move<0xB1, 0xF>(v, v); }  // quad_perm(1,0,3,2)
+__device__ __forceinline__ float lane_xor2(float v) { return dpp_move<0x4E, 0xF>(v, v); }  // quad_perm(2,3,0,1)
+__device__ __forceinline__ float lane_xor4(float v) {
+  const float t = dpp_move<0x104, 0x5>(v, v);  // row_shl:4 into lanes 0-3 and 8-11 of a row
+  return dpp_move<0x114, 0xA>(t, v);           // row_shr:4 into lanes 4-7 and 12-15
+}
+__device__ __forceinline__ float lane_xor8(float v) { return dpp_move<0x128, 0xF>(v, v); }  // row_ror:8
+
+// maximum of v over lanes l, l ^ 16, l ^ 32, l ^ 48: a row swap and a half
+// swap of two copies put each partner's value beside the lane's own
+__device__ __forceinline__ float max_xor16_32(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+}
+
 // binary16 bits of v >= 0 (nearest even), 65504 where the rounding would overflow
 __device__ __forceinline__ uint32_t f16_bits_saturating(float v) {
   return v >= 65520.0f ? 0x7BFFu : float_to_half_bits(v);
@@ -34,15 +62,14 @@ __device__ __forceinline__ uint32_t f16_bits_saturating(float v) {
 
 template <bool BF16>
 __global__ __launch_bounds__(kQzThreads) void quantize_q4k_kernel(const void* __restrict__ x,
-                                                                  uint8_t* __restrict__ w, int cols,
+                                                                  uint8_t* __restrict__ w,
                                                                   long long nblocks) {
   const int lane = threadIdx.x & 63;
   const long long blk = static_cast<long long>(blockIdx.x) * (kQzThreads / 64) + (threadIdx.x >> 6);
   if (blk >= nblocks) return;  // whole wavefronts; the kernel has no barrier
-  const int nb = cols >> 8;
-  const long long row = blk / nb;
-  const long long b = blk - row * nb;
-  const size_t e = static_cast<size_t>(row) * cols + static_cast<size_t>(b) * kQK + 4 * lane;
+  // rows are contiguous and a whole number of blocks long, so block blk holds
+  // values 256 blk .. 256 blk + 255 of the matrix
+  const size_t e = static_cast<size_t>(blk) * kQK + 4 * lane;
   float v[4];
   if constexpr (BF16) {
     const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(x) + e);
@@ -61,22 +88,19 @@ __global__ __launch_bounds__(kQzThreads) void quantize_q4k_kernel(const void* __
   // sub-block extrema over its 8 lanes, then the step and offset
   float mn = fminf(fminf(v[0], v[1]), fminf(v[2], v[3]));
   float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-#pragma unroll
-  for (int off = 1; off < 8; off <<= 1) {
-    mn = fminf(mn, __shfl_xor(mn, off, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  }
+  mn = fminf(mn, lane_xor1(mn));
+  mx = fmaxf(mx, lane_xor1(mx));
+  mn = fminf(mn, lane_xor2(mn));
+  mx = fmaxf(mx, lane_xor2(mx));
+  mn = fminf(mn, lane_xor4(mn));
+  mx = fmaxf(mx, lane_xor4(mx));
   const float lo = fminf(mn, 0.0f);
   const float o = 0.0f - lo;
   const float s = mx > lo ? (mx - lo) / 15.0f : 0.0f;
 
   // block scale and min
-  float smax = s, omax = o;
-#pragma unroll
-  for (int off = 8; off < 64; off <<= 1) {
-    smax = fmaxf(smax, __shfl_xor(smax, off, 64));
-    omax = fmaxf(omax, __shfl_xor(omax, off, 64));
-  }
+  const float smax = max_xor16_32(fmaxf(s, lane_xor8(s)));
+  const float omax = max_xor16_32(fmaxf(o, lane_xor8(o)));
   const uint32_t dbits = f16_bits_saturating(smax / 63.0f);
   const uint32_t mbits = f16_bits_saturating(omax / 63.0f);
   const float d = half_bits_to_float(dbits);
@@ -93,7 +117,7 @@ __global__ __launch_bounds__(kQzThreads) void quantize_q4k_kernel(const void* __
     const uint32_t q = ds > 0.0f ? static_cast<uint32_t>(fminf(fmaxf(rintf((v[r] + dm) / ds), 0.0f), 15.0f)) : 0u;
     qw |= q << (8 * r);
   }
-  const uint32_t hiw = static_cast<uint32_t>(__shfl_xor(static_cast<int>(qw), 8, 64));
+  const uint32_t hiw = __float_as_uint(lane_xor8(__uint_as_float(qw)));
   uint8_t* out = w + static_cast<size_t>(blk) * kBlockBytes;
   if ((lane & 8) == 0)
     *reinterpret_cast<uint32_t*>(out + 16 + 32 * (lane >> 4) + 4 * (lane & 7)) = qw | (hiw << 4);
@@ -130,9 +154,9 @@ hipError_t launch_quantize_q4k(const void* x, int x_bf16, int rows, int cols, ui
   if (groups > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(groups));
   if (x_bf16)
-    quantize_q4k_kernel<true><<<grid, dim3(kQzThreads), 0, stream>>>(x, w, cols, nblocks);
+    quantize_q4k_kernel<true><<<grid, dim3(kQzThreads), 0, stream>>>(x, w, nblocks);
   else
-    quantize_q4k_kernel<false><<<grid, dim3(kQzThreads), 0, stream>>>(x, w, cols, nblocks);
+    quantize_q4k_kernel<false><<<grid, dim3(kQzThreads), 0, stream>>>(x, w, nblocks);
   return hipGetLastError();
 }
 
