@@ -177,21 +177,24 @@ def decode_ffn(q4k, synth, reps=40):
     copies = rotated(cat)
     gb = q4k.q4k_weight_bytes(inter, hidden)
     out = {}
-    for m in (1, 4, 8):
-        x = torch.from_numpy(synth.activations(synth.DECODE_FFN_7B, m, hidden, True, sub=m)).cuda()
-        y = torch.empty((m, hidden), dtype=torch.float32, device="cuda")
-        ws = torch.empty(q4k.ffn_swiglu_q4k_workspace_bytes(m, hidden, inter), dtype=torch.uint8,
-                         device="cuda")
+    # f32 activations (the decode regime), then the Q8_1 decode regime
+    # (Q8_1 of x and h, integer-dot GEMVs; entries "q8_m1" ...)
+    for tag, regime in (("", q4k.Q4K_REGIME_DECODE), ("q8_", q4k.Q4K_REGIME_DECODE_Q8)):
+        for m in (1, 4, 8):
+            x = torch.from_numpy(synth.activations(synth.DECODE_FFN_7B, m, hidden, True, sub=m)).cuda()
+            y = torch.empty((m, hidden), dtype=torch.float32, device="cuda")
+            ws = torch.empty(q4k.ffn_swiglu_q4k_workspace_bytes(m, hidden, inter, 0, regime),
+                             dtype=torch.uint8, device="cuda")
 
-        def call(i):
-            c = copies[i % len(copies)]
-            q4k.ffn_swiglu_q4k(c[:gb], c[gb:2 * gb], c[2 * gb:], x, q4k.Q4K_F32, m, hidden, inter,
-                               y, ws)
+            def call(i, x=x, y=y, ws=ws, m=m, regime=regime):
+                c = copies[i % len(copies)]
+                q4k.ffn_swiglu_q4k(c[:gb], c[gb:2 * gb], c[2 * gb:], x, q4k.Q4K_F32, m, hidden, inter,
+                                   y, ws, regime=regime)
 
-        ms = timed_graph(call, reps, 5)
-        us = ms * 1e3 / reps
-        out[f"m{m}"] = dict(us_per_ffn=round(us, 2), tokens_per_s=round(m / (us * 1e-6), 1),
-                            weight_gbs=round(per_ffn / (us * 1e-6) / 1e9, 1))
+            ms = timed_graph(call, reps, 5)
+            us = ms * 1e3 / reps
+            out[f"{tag}m{m}"] = dict(us_per_ffn=round(us, 2), tokens_per_s=round(m / (us * 1e-6), 1),
+                                     weight_gbs=round(per_ffn / (us * 1e-6) / 1e9, 1))
     return out
 
 

@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     Q4K_REGIME_AUTO,
     Q4K_REGIME_DECODE,
     Q4K_REGIME_PREFILL,
+    Q4K_REGIME_DECODE_Q8,
     Q4KError,
     ffn_swiglu_q4k,
     ffn_swiglu_q4k_workspace_bytes,

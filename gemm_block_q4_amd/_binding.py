@@ -12,7 +12,7 @@ import ctypes
 import os
 
 Q4K_F32, Q4K_BF16 = 0, 1
-Q4K_REGIME_AUTO, Q4K_REGIME_DECODE, Q4K_REGIME_PREFILL = 0, 1, 2
+Q4K_REGIME_AUTO, Q4K_REGIME_DECODE, Q4K_REGIME_PREFILL, Q4K_REGIME_DECODE_Q8 = 0, 1, 2, 3
 Q4K_DECODE_MAX_TOKENS = 8
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -96,9 +96,9 @@ struct FfnLayout {
   size_t total = 0;
   // decode dense (and MoE: h and the pair outputs of every (token, slot) pair)
   size_t h = 0, y_pair = 0;
-  // prefill: Q8_1 of x and of h; the span qx .. qh (which includes h's
-  // m x inter f32 region, left unwritten) holds the down pass's k-split
-  // partial sums
+  // prefill and decode_q8: Q8_1 of x and of h, and h itself (decode_q8; the
+  // prefill pass leaves it unwritten, and the span qx .. qh holds the
+  // prefill down pass's k-split partial sums)
   size_t qx = 0, dx = 0, qh = 0, dh = 0;
 };
 
@@ -111,8 +111,10 @@ bool ffn_layout(int m, int hidden, int inter, int top_k, int regime, FfnLayout* 
   if (m < 1 || hidden < Q4K_QK || inter < Q4K_QK || hidden % Q4K_QK || inter % Q4K_QK) return false;
   if (top_k < 0 || top_k > 64) return false;
   regime = resolve_regime(regime, m);
-  if (regime != Q4K_REGIME_DECODE && regime != Q4K_REGIME_PREFILL) return false;
-  if (regime == Q4K_REGIME_DECODE && m > Q4K_DECODE_MAX_TOKENS) return false;
+  if (regime != Q4K_REGIME_DECODE && regime != Q4K_REGIME_PREFILL && regime != Q4K_REGIME_DECODE_Q8)
+    return false;
+  if ((regime == Q4K_REGIME_DECODE || regime == Q4K_REGIME_DECODE_Q8) && m > Q4K_DECODE_MAX_TOKENS)
+    return false;
   if (top_k > 0 && regime != Q4K_REGIME_DECODE) return false;
   const size_t M = static_cast<size_t>(m), H = static_cast<size_t>(hidden), I = static_cast<size_t>(inter);
   size_t off = 0;
@@ -289,11 +291,12 @@ int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int
     if (n_experts != 1 || (top_k != 0 && top_k != 1)) return Q4K_ERR_SHAPE;
     top_k = 0;
   }
-  if (regime < Q4K_REGIME_AUTO || regime > Q4K_REGIME_PREFILL) return Q4K_ERR_SHAPE;
+  if (regime < Q4K_REGIME_AUTO || regime > Q4K_REGIME_DECODE_Q8) return Q4K_ERR_SHAPE;
   const int reg = resolve_regime(regime, m);
-  if (reg == Q4K_REGIME_DECODE && m > Q4K_DECODE_MAX_TOKENS) return Q4K_ERR_SHAPE;
+  const bool decode = reg == Q4K_REGIME_DECODE || reg == Q4K_REGIME_DECODE_Q8;
+  if (decode && m > Q4K_DECODE_MAX_TOKENS) return Q4K_ERR_SHAPE;
   if (moe && reg != Q4K_REGIME_DECODE) return Q4K_ERR_SHAPE;
-  if (reg == Q4K_REGIME_DECODE && (hidden > kDecodeMaxK || inter > kDecodeMaxK)) return Q4K_ERR_SHAPE;
+  if (decode && (hidden > kDecodeMaxK || inter > kDecodeMaxK)) return Q4K_ERR_SHAPE;
   if (reg == Q4K_REGIME_PREFILL && (m > kPrefillMaxM || hidden > kPrefillMaxK || inter > kPrefillMaxK))
     return Q4K_ERR_SHAPE;
   size_t gu_bytes, dn_bytes;
@@ -394,14 +397,25 @@ int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int
     return launch_status(launch_gemv(dn, s));
   }
 
-  // Prefill: x -> Q8_1 -> MMQ gate/up with silu*mul and Q8_1(h) in its
-  // epilogue -> MMQ down (h itself is never stored).
   int8_t* qx = reinterpret_cast<int8_t*>(ws + L.qx);
   uint32_t* dx = reinterpret_cast<uint32_t*>(ws + L.dx);
   int8_t* qh = reinterpret_cast<int8_t*>(ws + L.qh);
   uint32_t* dh = reinterpret_cast<uint32_t*>(ws + L.dh);
   hipError_t e = launch_q8_1_quantize(x, x_dtype == Q4K_BF16, m, hidden, qx, dx, s);
   if (e != hipSuccess) return Q4K_ERR_LAUNCH;
+
+  if (reg == Q4K_REGIME_DECODE_Q8) {
+    // x -> Q8_1 -> gate/up integer-dot GEMV with silu*mul -> h -> Q8_1 ->
+    // down integer-dot GEMV
+    if ((e = launch_q8_gemv_gu(static_cast<const uint8_t*>(w_gate), static_cast<const uint8_t*>(w_up), qx,
+                               dx, h, m, inter, hidden, s)) != hipSuccess)
+      return Q4K_ERR_LAUNCH;
+    if ((e = launch_q8_1_quantize(h, 0, m, inter, qh, dh, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
+    return launch_status(launch_q8_gemv(static_cast<const uint8_t*>(w_down), qh, dh, y, m, hidden, inter, s));
+  }
+
+  // Prefill: x -> Q8_1 -> MMQ gate/up with silu*mul and Q8_1(h) in its
+  // epilogue -> MMQ down (h itself is never stored).
   MmqArgs gu{};
   gu.w = static_cast<const uint8_t*>(w_gate);
   gu.w_up = static_cast<const uint8_t*>(w_up);

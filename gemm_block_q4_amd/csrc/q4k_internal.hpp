@@ -77,6 +77,9 @@ hipError_t launch_mmq(const MmqArgs& a, hipStream_t stream);
 // Q4_K rows, 1 <= m <= 8, 256 <= k <= 32768 (validated by the caller).
 hipError_t launch_q8_gemv(const uint8_t* w, const int8_t* qs, const uint32_t* ds, float* y, int m,
                           int n, int k, hipStream_t stream);
+// Gate/up form: h [m][n] = silu(gate . x) * (up . x), both matrices [n][k].
+hipError_t launch_q8_gemv_gu(const uint8_t* w_gate, const uint8_t* w_up, const int8_t* qs,
+                             const uint32_t* ds, float* h, int m, int n, int k, hipStream_t stream);
 
 // Number of k splits (1 .. max_splits) for the single-matrix MMQ pass of an
 // m x n x k product on a device with `cus` compute units: the one that

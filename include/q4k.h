@@ -81,7 +81,8 @@ typedef enum { Q4K_F32 = 0, Q4K_BF16 = 1 } q4k_dtype;
 typedef enum {
   Q4K_REGIME_AUTO = 0,    /* decode when m <= Q4K_DECODE_MAX_TOKENS, else prefill */
   Q4K_REGIME_DECODE = 1,  /* f32 activations, dequant-fused GEMV */
-  Q4K_REGIME_PREFILL = 2  /* Q8_1 activations, integer MMQ */
+  Q4K_REGIME_PREFILL = 2, /* Q8_1 activations, integer MMQ */
+  Q4K_REGIME_DECODE_Q8 = 3 /* Q8_1 activations, integer-dot GEMV (m <= 8, dense only) */
 } q4k_regime;
 
 /* Host.  Bytes of a Q4_K matrix [rows][cols]: rows * (cols/256) * 144
@@ -194,9 +195,12 @@ size_t ffn_swiglu_q4k_workspace_bytes(int m, int hidden, int inter, int top_k, i
    [0, n_experts) contributes nothing (device data is not read back).
    Regime: decode = f32 activations through the dequant-fused GEMV (gate and
    up in one pass with silu*mul fused); prefill = x -> Q8_1 -> MMQ gate/up
-   with fused silu*mul -> h -> Q8_1 -> MMQ down.  MoE needs the decode regime
+   with fused silu*mul -> h -> Q8_1 -> MMQ down; decode_q8 ("ffn.rs",
+   fused_ffn_swiglu_gpu_true_dp4a) = x -> Q8_1 -> integer-dot gate/up GEMV
+   with fused silu*mul -> h (f32) -> Q8_1 -> integer-dot down GEMV, the
+   prefill arithmetic for 1 <= m <= 8 tokens.  MoE needs the decode regime
    (m <= 8).  hidden, inter: multiples of 256 (at most 32768 in the decode
-   regime, at most 2^20 in the prefill regime).
+   regimes, at most 2^20 in the prefill regime).
    workspace: device, at least ffn_swiglu_q4k_workspace_bytes(...) bytes.
    Errors: Q4K_ERR_NULL, Q4K_ERR_SHAPE, Q4K_ERR_ALIGN, Q4K_ERR_OVERFLOW,
    Q4K_ERR_WORKSPACE, Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */

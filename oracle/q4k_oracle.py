@@ -419,6 +419,8 @@ def ffn_prefill(w_gate, w_up, w_down, hidden: int, inter: int, x: np.ndarray,
     and the SwiGLU are f64; ``h`` is rounded to f32 before its quantisation
     (the Q8_1 encoding is defined on binary32 input).  Every step is per
     token, so ``tokens`` may select a subset; returns f64 [len, hidden].
+    The DP4A decode FFN of "ffn.rs" (``fused_ffn_swiglu_gpu_true_dp4a``)
+    computes the same steps for a few tokens, so this is its oracle too.
     """
     x = np.asarray(x, dtype=np.float32)
     if tokens is None:

@@ -117,6 +117,15 @@ def test_ffn_validation(lib):
     assert f(P, P, P, 4, P, 0, 1, 256, 768, P, P, 2, 2, P, P, ws, None) == 2
     # decode regime forced with too many tokens
     assert f(P, P, P, 1, P, 0, 9, 256, 768, None, None, 0, 1, P, P, ws, None) == 2
+    # Q8_1 decode regime: at most 8 tokens, dense only, k bound of the decode GEMVs
+    assert f(P, P, P, 1, P, 0, 9, 256, 768, None, None, 0, 3, P, P, ws, None) == 2
+    assert f(P, P, P, 4, P, 0, 1, 256, 768, P, P, 2, 3, P, P, ws, None) == 2
+    assert f(P, P, P, 1, P, 0, 1, 256, 32768 + 256, None, None, 0, 3, P, P, 1 << 40, None) == 2
+    # unknown regime
+    assert f(P, P, P, 1, P, 0, 1, 256, 768, None, None, 0, 4, P, P, ws, None) == 2
+    # Q8_1 decode regime with the f32 decode regime's (smaller) workspace
+    assert lib.ffn_swiglu_q4k_workspace_bytes(1, 256, 768, 0, 3) > ws
+    assert f(P, P, P, 1, P, 0, 1, 256, 768, None, None, 0, 3, P, P, ws, None) == 5
     # workspace too small / missing
     assert f(P, P, P, 1, P, 0, 1, 256, 768, None, None, 0, 0, P, P, ws - 1, None) == 5
     assert f(P, P, P, 1, P, 0, 1, 256, 768, None, None, 0, 0, P, None, ws, None) == 5
@@ -132,3 +141,8 @@ def test_workspace_sizes(lib):
     assert w(0, 256, 256, 0, 0) == 0
     assert w(9, 256, 256, 0, 1) == 0      # decode regime caps m at 8
     assert w(4, 256, 256, 2, 2) == 0      # MoE is decode-only
+    # Q8_1 decode: Q8_1 of x and of h, and h in f32
+    assert w(8, 4096, 11008, 0, 3) >= 8 * (4096 + 4096 // 32 * 4 + 11008 * 4 + 11008 + 11008 // 32 * 4)
+    assert w(9, 256, 256, 0, 3) == 0
+    assert w(4, 256, 256, 2, 3) == 0      # MoE runs in the f32 decode regime only
+    assert w(1, 256, 256, 0, 4) == 0

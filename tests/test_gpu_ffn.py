@@ -90,6 +90,31 @@ def test_decode_regime_forced_m8_matches(lib):
     assert orc.relative_l2(y, orc.ffn_decode(wg, wu, wd, hidden, inter, x)) <= TOL
 
 
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_decode_q8_ffn_7b(lib, decode7b, m):
+    # Q8_1 decode regime: the prefill arithmetic (Q8_1 of x and of h) on the
+    # integer-dot GEMVs
+    say(f"ffn decode_q8 4096/11008 m={m}")
+    wg, wu, wd = decode7b
+    x = synth.activations(synth.DECODE_FFN_7B, m, 4096, outliers=True, sub=m)
+    y = ffn_gpu(lib, wg, wu, wd, x, 4096, 11008, regime=q4kmod.Q4K_REGIME_DECODE_Q8)
+    assert orc.relative_l2(y, orc.ffn_prefill(wg, wu, wd, 4096, 11008, x)) <= TOL
+
+
+@pytest.mark.parametrize("m,hidden,inter,bf16", [
+    (2, 512, 768, True), (3, 4608, 512, False),   # gate/up rows span two wavefronts
+    (5, 512, 8448, True),                          # down rows span three
+    (7, 256, 256, False), (1, 8192, 1024, True), (6, 1024, 2816, False)])
+def test_decode_q8_ffn_shapes(lib, m, hidden, inter, bf16):
+    say(f"ffn decode_q8 {hidden}/{inter} m={m} bf16={bf16}")
+    wg, wu, wd = synth.dense_ffn_weights(94, hidden, inter)
+    x = synth.activations(94, m, hidden, outliers=True, sub=m)
+    y = ffn_gpu(lib, wg, wu, wd, x, hidden, inter, regime=q4kmod.Q4K_REGIME_DECODE_Q8, bf16=bf16)
+    xr = synth.bf16_bits_to_f32(synth.to_bf16_bits(x)) if bf16 else x
+    assert orc.relative_l2(y, orc.ffn_prefill(wg, wu, wd, hidden, inter, xr)) <= TOL
+    assert np.all(np.isfinite(y))
+
+
 @pytest.fixture(scope="module")
 def prefill_weights():
     return synth.dense_ffn_weights(synth.PREFILL_FFN, 5120, 17408)
