@@ -49,6 +49,25 @@ def random_q4k(g: np.random.Generator, rows: int, cols: int,
     return out.reshape(-1)
 
 
+Q6K_BLOCK_BYTES = 210
+
+
+def random_q6k(g: np.random.Generator, rows: int, cols: int,
+               dlo: float = 1e-3, dhi: float = 1e-2) -> np.ndarray:
+    """Random block_q6_K matrix [rows, cols] as uint8 [rows * cols/256 * 210]:
+    208 uniform bytes (the 4-bit and 2-bit quant fields, then 16 int8 scales)
+    and a binary16 d drawn uniform on [dlo, dhi]."""
+    if cols % BLOCK_WEIGHTS:
+        raise ValueError("cols must be a multiple of 256")
+    nb = rows * (cols // BLOCK_WEIGHTS)
+    body = g.integers(0, 256, (nb, 208), dtype=np.uint8)
+    d = g.uniform(dlo, dhi, nb).astype(np.float32).astype(np.float16)
+    out = np.empty((nb, Q6K_BLOCK_BYTES), dtype=np.uint8)
+    out[:, :208] = body
+    out[:, 208:210] = d.view(np.uint8).reshape(nb, 2)
+    return out.reshape(-1)
+
+
 def activations(workload: int, m: int, k: int, outliers: bool, sub: int = 0,
                 seed: int = 0) -> np.ndarray:
     """f32 [m, k] from N(0, 1); with ``outliers`` exactly max(1, round(0.001*m*k))
@@ -94,6 +113,7 @@ GEMV_SWEEP = 1        # (n, k) in {(4096, 4096), (11008, 4096), (4096, 11008)}, 
 DECODE_FFN_7B = 2     # hidden 4096, inter 11008, 1/4/8 tokens, outliers
 PREFILL_FFN = 3       # hidden 5120, inter 17408, 512/2048 tokens, bf16, outliers
 MOE_DECODE = 4        # 64 experts, top-8, 4 tokens, hidden 2048, inter 768
+LM_HEAD = 5           # Q6_K LM head GEMV: vocab 32000 x hidden 4096, 1 token
 
 GEMV_SWEEP_SHAPES = ((4096, 4096), (11008, 4096), (4096, 11008))
 
@@ -119,3 +139,10 @@ def gemv_sweep_case(shape_index: int, m: int = 1, seed: int = 0):
     w = random_q4k(rng(GEMV_SWEEP, TENSOR_GATE, shape_index, seed), n, k)
     x = activations(GEMV_SWEEP, m, k, outliers=False, sub=shape_index, seed=seed)
     return n, k, w, x
+
+
+def lm_head_case(vocab: int = 32000, hidden: int = 4096, sub: int = 0, seed: int = 0):
+    """Q6_K LM head [vocab, hidden] and one N(0, 1) token."""
+    w = random_q6k(rng(LM_HEAD, TENSOR_GATE, sub, seed), vocab, hidden)
+    x = activations(LM_HEAD, 1, hidden, outliers=False, sub=sub, seed=seed)
+    return w, x
