@@ -251,6 +251,28 @@ def quantize_q4k(q4k, synth):
     return res
 
 
+def lm_head_q6k(q4k, synth):
+    """Q6_K LM head GEMV (q6k_gemv), vocab 32000 x hidden 4096, one token:
+    average launch time over a graph of launches on rotated weight copies
+    (>= 1 GiB), and effective weight-GB/s (210 B per 256 weights)."""
+    import torch
+    n, k = 32000, 4096
+    w, x = synth.lm_head_case(n, k)
+    copies = rotated(w)
+    xd = torch.from_numpy(x.reshape(-1)).cuda()
+    y = torch.empty(n, dtype=torch.float32, device="cuda")
+    nbytes = q4k.q6k_weight_bytes(n, k)
+
+    def call(i):
+        q4k.q6k_gemv(copies[i % len(copies)], xd, y, n, k)
+
+    reps = 4 * len(copies)
+    ms = timed_graph(call, reps, len(copies))
+    us = ms * 1e3 / reps
+    return dict(us=round(us, 2), weight_gbs=round(nbytes / (us * 1e-6) / 1e9, 1),
+                frac_hbm_peak=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
+
+
 def prefill_ffn(q4k, synth, reps=4):
     import torch
     hidden, inter = 5120, 17408
@@ -383,6 +405,8 @@ def main():
         secondary["q8_gemv_sweep"] = q8_gemv(q4k, synth)
         log("bench: Q4_K quantiser")
         secondary["q4k_quantize_11008_4096"] = quantize_q4k(q4k, synth)
+        log("bench: Q6_K LM head GEMV")
+        secondary["lm_head_q6k_32000_4096"] = lm_head_q6k(q4k, synth)
 
     cpu = None
     if not args.skip_cpu:

@@ -24,5 +24,7 @@ from ._binding import (  # noqa: F401
     q4k_quantize,
     q4k_test_mmq_partials,
     q4k_weight_bytes,
+    q6k_gemv,
+    q6k_weight_bytes,
     q8_1_quantize,
 )

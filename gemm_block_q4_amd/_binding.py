@@ -40,6 +40,8 @@ _SIGNATURES = {
     "q4k_test_mmq_partials": (_I, [_VP, _VP, _I, _I, _I, _VP, _VP]),
     "q4k_q8_gemv": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _VP]),
     "q4k_quantize": (_I, [_VP, _I, _I, _I, _VP, _VP]),
+    "q6k_weight_bytes": (_SZ, [_I, _I]),
+    "q6k_gemv": (_I, [_VP, _VP, _VP, _I, _I, _VP]),
     "ffn_swiglu_q4k_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "ffn_swiglu_q4k": (_I, [_VP, _VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP, _I, _I, _VP,
                             _VP, _SZ, _VP]),
@@ -93,6 +95,10 @@ def q4k_weight_bytes(rows: int, cols: int) -> int:
     return int(load_library().q4k_weight_bytes(rows, cols))
 
 
+def q6k_weight_bytes(rows: int, cols: int) -> int:
+    return int(load_library().q6k_weight_bytes(rows, cols))
+
+
 def ffn_swiglu_q4k_workspace_bytes(m: int, hidden: int, inter: int, top_k: int = 0,
                                    regime: int = Q4K_REGIME_AUTO) -> int:
     return int(load_library().ffn_swiglu_q4k_workspace_bytes(m, hidden, inter, top_k, regime))
@@ -124,6 +130,11 @@ def q4k_q8_gemv(w, qs, ds, y, m: int, n: int, k: int, stream=None) -> None:
     """y[m, n] = reference dot of Q8_1 rows (qs, ds) with the Q4_K rows, m <= 8."""
     _check(load_library().q4k_q8_gemv(_ptr(w), _ptr(qs), _ptr(ds), _ptr(y), m, n, k,
                                       _stream(stream)))
+
+
+def q6k_gemv(w, x, y, n: int, k: int, stream=None) -> None:
+    """y[n] = dequant(w)[n, k] @ x[k] for Q6_K weights w (one f32 token)."""
+    _check(load_library().q6k_gemv(_ptr(w), _ptr(x), _ptr(y), n, k, _stream(stream)))
 
 
 def q4k_test_mmq_partials(w, qs, m: int, n: int, k: int, partials, stream=None) -> None:

@@ -20,6 +20,7 @@ namespace {
 
 constexpr size_t kAlign = 16;
 constexpr size_t kWsAlign = 256;
+constexpr size_t kQ6kBlockBytes = 210;  // block_q6_K
 constexpr int kMaxDevices = 64;
 // Decode path: the per-token sub-block sums and the per-row partials live in
 // LDS, which bounds the reduction length.
@@ -262,6 +263,28 @@ int q4k_q8_gemv(const void* w, const int8_t* qs, const uint32_t* ds, float* y, i
   if ((st = check_device())) return st;
   return launch_status(launch_q8_gemv(static_cast<const uint8_t*>(w), qs, ds, y, m, n, k,
                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t q6k_weight_bytes(int rows, int cols) {
+  if (rows < 0 || cols < 0 || cols % Q4K_QK != 0) return 0;
+  size_t blocks, bytes;
+  if (!mul_ok(static_cast<size_t>(rows), static_cast<size_t>(cols / Q4K_QK), &blocks)) return 0;
+  if (!mul_ok(blocks, kQ6kBlockBytes, &bytes)) return 0;
+  return bytes;
+}
+
+int q6k_gemv(const void* w, const float* x, float* y, int n, int k, void* stream) {
+  if (!w || !x || !y) return Q4K_ERR_NULL;
+  if (n < 1 || k < Q4K_QK || k % Q4K_QK != 0 || k > kDecodeMaxK) return Q4K_ERR_SHAPE;
+  size_t blocks, bytes;
+  if (!mul_ok(static_cast<size_t>(n), static_cast<size_t>(k / Q4K_QK), &blocks) ||
+      blocks > static_cast<size_t>(INT32_MAX) || !mul_ok(blocks, kQ6kBlockBytes, &bytes))
+    return Q4K_ERR_OVERFLOW;
+  if (!aligned(w, kAlign) || !aligned(x, kAlign) || !aligned(y, 4)) return Q4K_ERR_ALIGN;
+  int st = check_device();
+  if (st) return st;
+  return launch_status(launch_q6k_gemv(static_cast<const uint8_t*>(w), x, y, n, k,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 int q4k_test_mmq_partials(const void* w, const int8_t* qs, int m, int n, int k,

@@ -77,6 +77,9 @@ hipError_t launch_mmq(const MmqArgs& a, hipStream_t stream);
 // Q4_K rows, 1 <= m <= 8, 256 <= k <= 32768 (validated by the caller).
 hipError_t launch_q8_gemv(const uint8_t* w, const int8_t* qs, const uint32_t* ds, float* y, int m,
                           int n, int k, hipStream_t stream);
+// Q6_K GEMV, one f32 token: y [n] = dequant(w) [n][k] . x, 256 <= k <= 32768.
+hipError_t launch_q6k_gemv(const uint8_t* w, const float* x, float* y, int n, int k, hipStream_t stream);
+
 // Gate/up form: h [m][n] = silu(gate . x) * (up . x), both matrices [n][k].
 hipError_t launch_q8_gemv_gu(const uint8_t* w_gate, const uint8_t* w_up, const int8_t* qs,
                              const uint32_t* ds, float* h, int m, int n, int k, hipStream_t stream);

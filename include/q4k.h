@@ -168,6 +168,25 @@ int q4k_mmq(const void* w, const int8_t* qs, const uint32_t* ds, float* y, int m
 int q4k_q8_gemv(const void* w, const int8_t* qs, const uint32_t* ds, float* y, int m, int n,
                 int k, void* stream);
 
+/* Host.  Bytes of a Q6_K matrix [rows][cols]: rows * (cols/256) * 210
+   (GGML's block_q6_K: 128 bytes of low 4 bits, 64 of high 2 bits, 16 int8
+   scales, an fp16 d).  Returns 0 when rows < 0, cols < 0, cols % 256 != 0 or
+   the size overflows. */
+size_t q6k_weight_bytes(int rows, int cols);
+
+/* Q6_K GEMV for the LM head ("q4k_gemv_cached_uses.rs",
+   q6k_gemv_cached_async: the Q4_K GEMV for Q6_K weights, one f32 token):
+     y[j] = sum_i dequant(w)[j][i] * x[i]   for j < n,
+   with weight i of a block = d * scales[i/16] * (u - 32), u its 6-bit value
+   (low nibble of ql[64h + 32(r&1) + l] for quarter r < 2 of half h, high
+   nibble for r >= 2, high 2 bits = bits 2r..2r+1 of qh[32h + l]).
+   w: device, block_q6_K [n][k/256] (210-byte blocks, contiguous rows), 16-byte
+   aligned; x: device f32 [k], 16-byte aligned; y: device f32 [n], overwritten.
+   n >= 1, 256 <= k <= 32768, k % 256 == 0.  Products and sums in f32.
+   Errors: Q4K_ERR_NULL, Q4K_ERR_SHAPE, Q4K_ERR_ALIGN, Q4K_ERR_OVERFLOW,
+   Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */
+int q6k_gemv(const void* w, const float* x, float* y, int n, int k, void* stream);
+
 /* Test hook on the same device code as q4k_mmq: writes the integer partials
    partials[t][j][b] = P[t][j][b] (int32 [m][n][k/32], device) instead of y.
    Same shape rules as q4k_mmq; meant for small shapes. */

@@ -34,7 +34,8 @@ def test_exports_every_declared_function(lib):
     names = declared_functions()
     assert {"q4k_gemv", "q8_1_quantize", "q4k_mmq", "ffn_swiglu_q4k", "q4k_weight_bytes",
             "q4k_status_string", "ffn_swiglu_q4k_workspace_bytes",
-            "q4k_test_mmq_partials", "q4k_q8_gemv", "q4k_quantize"} <= set(names)
+            "q4k_test_mmq_partials", "q4k_q8_gemv", "q4k_quantize", "q6k_gemv",
+            "q6k_weight_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -146,3 +147,21 @@ def test_workspace_sizes(lib):
     assert w(9, 256, 256, 0, 3) == 0
     assert w(4, 256, 256, 2, 3) == 0      # MoE runs in the f32 decode regime only
     assert w(1, 256, 256, 0, 4) == 0
+
+
+def test_q6k_sizes_and_validation(lib):
+    from oracle import q6k_oracle as q6
+    for rows, cols in ((32000, 4096), (1, 256), (7, 11008)):
+        assert lib.q6k_weight_bytes(rows, cols) == q6.q6k_weight_bytes(rows, cols)
+    assert lib.q6k_weight_bytes(4, 300) == 0
+    assert lib.q6k_weight_bytes(-1, 256) == 0
+    g = lib.q6k_gemv
+    assert g(None, P, P, 10, 256, None) == 1
+    assert g(P, None, P, 10, 256, None) == 1
+    assert g(P, P, P, 0, 256, None) == 2           # no rows
+    assert g(P, P, P, 10, 300, None) == 2          # k not a multiple of 256
+    assert g(P, P, P, 10, 32768 + 256, None) == 2  # k above the decode bound
+    assert g(P + 2, P, P, 10, 256, None) == 3      # weights need 16 bytes
+    assert g(P, P + 4, P, 10, 256, None) == 3      # x needs 16 bytes
+    assert g(P, P, P + 2, 10, 256, None) == 3
+    assert g(P, P, P, 1 << 30, 32768, None) == 4   # block count overflows
