@@ -315,11 +315,12 @@ Q6Geo make_q6_geo(int n, int k) {
   const int S = 4 * (k / kQK);
   g.wr = (S + 63) / 64;
   g.rs = g.wr >= 4 ? 1 : (4 + g.wr - 1) / g.wr;
-  // about two workgroups per compute unit (512), whole slots
-  long long want = (static_cast<long long>(n) + 511) / 512;
-  if (want < g.rs) want = g.rs;
+  // about one workgroup per compute unit (256), each slot a whole number of
+  // prefetch groups
+  const int unit = g.rs * kQ6PF;
+  long long want = (static_cast<long long>(n) + 255) / 256;
   if (want > kQ6MaxRowsPerGroup) want = kQ6MaxRowsPerGroup;
-  g.rpg = static_cast<int>((want + g.rs - 1) / g.rs * g.rs);
+  g.rpg = static_cast<int>((want + unit - 1) / unit * unit);
   return g;
 }
 
