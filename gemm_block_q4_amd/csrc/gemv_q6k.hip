@@ -20,19 +20,20 @@
 // of its four 16-weight sub-blocks, a sub-block's sum (u - 32) x is
 // 2^(e-21) (sum u X - 32 SX) and sum u X takes three v_dot4 per four weights
 // (v_dot4_u32_u8 on the low planes, v_dot4_i32_i8 on the top one; u < 64).
-// A block starts at a multiple
-// of 210 bytes, i.e. only 2-byte aligned: the four lanes of a block (a lane
-// quad) load the aligned dwords around their fields and shift them into place
-// with v_alignbyte.  Each lane loads its 32 ql bytes and 32 qh bytes (eight
-// dwords each); the ninth dword a misaligned window needs is the first dword
-// of a quad-mate's window, and the 16 scale bytes are one dword per lane,
-// both passed around the quad by DPP.  The last dword of the block (scales
-// 14-15 and d) or, for a dword-aligned block, d alone is one more load, so
-// no load reaches past the block and every load instruction of a wavefront
-// touches few cache lines.  A wavefront covers 16
-// consecutive blocks of a row; wider rows span several wavefronts, whose sums
-// meet in LDS.  PF rows are in flight per wavefront; the reduction order is
-// fixed (deterministic).
+//
+// Loads.  A block starts at a multiple of 210 bytes, i.e. only 2-byte
+// aligned: the four lanes of a block (a lane quad) load the aligned dwords
+// around their fields and shift them into place with v_alignbyte.  Each lane
+// loads its 32 ql bytes and 32 qh bytes (eight dwords each); the ninth dword
+// a misaligned window needs is the first dword of a quad-mate's window, and
+// the 16 scale bytes are one dword per lane, both passed around the quad by
+// DPP.  The last dword of the block (scales 14-15 and d) or, for a
+// dword-aligned block, d alone is one more load, so no load reaches past the
+// block and every load instruction of a wavefront touches few cache lines.
+// A wavefront covers 16 consecutive blocks of a row; wider rows span several
+// wavefronts, whose sums meet in LDS.  PF rows are in flight per wavefront,
+// one workgroup per compute unit (more rows in flight measured slower); the
+// reduction order is fixed (deterministic).
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
 
