@@ -273,6 +273,32 @@ def lm_head_q6k(q4k, synth):
                 frac_hbm_peak=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
 
 
+def mmq_store(q4k, synth, reps=4):
+    """Single-matrix MMQ (the prefill down projection's shape, [5120, 17408],
+    2048 tokens, no k split) with the f32 store (q4k_mmq) and the fused
+    bfloat16 store (q4k_mmq_bf16): average launch time over a graph of
+    launches on rotated weight copies, and TOPS."""
+    import torch
+    n, k, m = 5120, 17408, 2048
+    w = synth.random_q4k(synth.rng(synth.PREFILL_FFN, 3, 7), n, k)
+    copies = rotated(w, max_copies=7)
+    x = torch.from_numpy(synth.activations(synth.PREFILL_FFN, m, k, True, sub=7)).cuda()
+    qs = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    ds = torch.empty((m, k // 32), dtype=torch.int32, device="cuda")
+    q4k.q8_1_quantize(x, q4k.Q4K_F32, m, k, qs, ds)
+    y32 = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    y16 = torch.empty((m, n), dtype=torch.int16, device="cuda")
+    out = {}
+    for name, fn, y in (("f32", q4k.q4k_mmq, y32), ("bf16", q4k.q4k_mmq_bf16, y16)):
+        def call(i, fn=fn, y=y):
+            fn(copies[i % len(copies)], qs, ds, y, m, n, k)
+
+        ms = timed_graph(call, reps, 1)
+        us = ms * 1e3 / reps
+        out[name] = dict(us=round(us, 1), tops=round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1))
+    return out
+
+
 def prefill_ffn(q4k, synth, reps=4):
     import torch
     hidden, inter = 5120, 17408
@@ -405,6 +431,8 @@ def main():
         secondary["q8_gemv_sweep"] = q8_gemv(q4k, synth)
         log("bench: Q4_K quantiser")
         secondary["q4k_quantize_11008_4096"] = quantize_q4k(q4k, synth)
+        log("bench: MMQ f32 and bf16 stores")
+        secondary["mmq_store_5120_17408_m2048"] = mmq_store(q4k, synth)
         log("bench: Q6_K LM head GEMV")
         secondary["lm_head_q6k_32000_4096"] = lm_head_q6k(q4k, synth)
 

@@ -20,6 +20,7 @@ from ._binding import (  # noqa: F401
     load_library,
     q4k_gemv,
     q4k_mmq,
+    q4k_mmq_bf16,
     q4k_q8_gemv,
     q4k_quantize,
     q4k_test_mmq_partials,

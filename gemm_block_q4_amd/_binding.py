@@ -37,6 +37,7 @@ _SIGNATURES = {
     "q4k_gemv": (_I, [_VP, _VP, _VP, _I, _I, _I, _VP]),
     "q8_1_quantize": (_I, [_VP, _I, _I, _I, _VP, _VP, _VP]),
     "q4k_mmq": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _VP]),
+    "q4k_mmq_bf16": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _VP]),
     "q4k_test_mmq_partials": (_I, [_VP, _VP, _I, _I, _I, _VP, _VP]),
     "q4k_q8_gemv": (_I, [_VP, _VP, _VP, _VP, _I, _I, _I, _VP]),
     "q4k_quantize": (_I, [_VP, _I, _I, _I, _VP, _VP]),
@@ -119,6 +120,12 @@ def q8_1_quantize(x, x_dtype: int, m: int, k: int, qs, ds, stream=None) -> None:
 def q4k_mmq(w, qs, ds, y, m: int, n: int, k: int, stream=None) -> None:
     _check(load_library().q4k_mmq(_ptr(w), _ptr(qs), _ptr(ds), _ptr(y), m, n, k,
                                   _stream(stream)))
+
+
+def q4k_mmq_bf16(w, qs, ds, y, m: int, n: int, k: int, stream=None) -> None:
+    """q4k_mmq with the result stored as bfloat16 bits (y: int16 or uint16 [m, n])."""
+    _check(load_library().q4k_mmq_bf16(_ptr(w), _ptr(qs), _ptr(ds), _ptr(y), m, n, k,
+                                       _stream(stream)))
 
 
 def q4k_quantize(x, x_dtype: int, rows: int, cols: int, w, stream=None) -> None:

@@ -218,9 +218,9 @@ int q4k_quantize(const void* x, int x_dtype, int rows, int cols, void* w, void* 
                                            static_cast<hipStream_t>(stream)));
 }
 
-static int mmq_common(const void* w, const int8_t* qs, const uint32_t* ds, float* y,
+static int mmq_common(const void* w, const int8_t* qs, const uint32_t* ds, float* y, uint16_t* y_bf16,
                       int32_t* partials, int m, int n, int k, void* stream) {
-  if (!w || !qs || (!partials && (!ds || !y))) return Q4K_ERR_NULL;
+  if (!w || !qs || (!partials && (!ds || (!y && !y_bf16)))) return Q4K_ERR_NULL;
   if (m < 1 || m > kPrefillMaxM || k > kPrefillMaxK) return Q4K_ERR_SHAPE;
   size_t wbytes;
   int st = check_matrix(n, k, &wbytes);
@@ -231,7 +231,7 @@ static int mmq_common(const void* w, const int8_t* qs, const uint32_t* ds, float
     if (!mul_ok(static_cast<size_t>(m) * static_cast<size_t>(n), static_cast<size_t>(k / 32), &e)) return Q4K_ERR_OVERFLOW;
   }
   if (!aligned(w, kAlign) || !aligned(qs, kAlign) || (ds && !aligned(ds, 4)) ||
-      (y && !aligned(y, 4)) || (partials && !aligned(partials, 4)))
+      (y && !aligned(y, 4)) || (y_bf16 && !aligned(y_bf16, 2)) || (partials && !aligned(partials, 4)))
     return Q4K_ERR_ALIGN;
   if ((st = check_device())) return st;
   MmqArgs a{};
@@ -239,6 +239,7 @@ static int mmq_common(const void* w, const int8_t* qs, const uint32_t* ds, float
   a.qs = qs;
   a.ds = ds;
   a.y = y;
+  a.y_bf16 = y_bf16;
   a.partials = partials;
   a.m = m;
   a.n = n;
@@ -248,7 +249,13 @@ static int mmq_common(const void* w, const int8_t* qs, const uint32_t* ds, float
 
 int q4k_mmq(const void* w, const int8_t* qs, const uint32_t* ds, float* y, int m, int n, int k,
             void* stream) {
-  return mmq_common(w, qs, ds, y, nullptr, m, n, k, stream);
+  return mmq_common(w, qs, ds, y, nullptr, nullptr, m, n, k, stream);
+}
+
+int q4k_mmq_bf16(const void* w, const int8_t* qs, const uint32_t* ds, uint16_t* y, int m, int n, int k,
+                 void* stream) {
+  if (!y) return Q4K_ERR_NULL;
+  return mmq_common(w, qs, ds, nullptr, y, nullptr, m, n, k, stream);
 }
 
 int q4k_q8_gemv(const void* w, const int8_t* qs, const uint32_t* ds, float* y, int m, int n, int k,
@@ -290,7 +297,7 @@ int q6k_gemv(const void* w, const float* x, float* y, int n, int k, void* stream
 int q4k_test_mmq_partials(const void* w, const int8_t* qs, int m, int n, int k,
                           int32_t* partials, void* stream) {
   if (!partials) return Q4K_ERR_NULL;
-  return mmq_common(w, qs, nullptr, nullptr, partials, m, n, k, stream);
+  return mmq_common(w, qs, nullptr, nullptr, nullptr, partials, m, n, k, stream);
 }
 
 size_t ffn_swiglu_q4k_workspace_bytes(int m, int hidden, int inter, int top_k, int regime) {

@@ -459,16 +459,28 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
   if constexpr (!PARTIALS) {
     // lane holds token xtok and, per tile, rows 8*(i/4) + 4*kh + i%4
     if (xtok < toks) {
-      float* yrow = a.y + blockIdx.z * a.split_stride + static_cast<size_t>(t0 + xtok) * a.n;
+      const size_t roff = blockIdx.z * a.split_stride + static_cast<size_t>(t0 + xtok) * a.n;
       if constexpr (GU) {
         if (a.q_out == nullptr) {
+          float* yrow = a.y + roff;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int r = wn * 32 + 8 * (i >> 2) + 4 * kh + (i & 3);
             if (r < rows) yrow[n0 + r] = silu_mul(acc[0][i] - accm[0][i], acc[1][i] - accm[1][i]);
           }
         }
+      } else if (a.y_bf16 != nullptr) {
+        // the result stored as bfloat16 straight from the tile
+        uint16_t* brow = a.y_bf16 + roff;
+#pragma unroll
+        for (int wt = 0; wt < 2; ++wt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = wn * 64 + wt * 32 + 8 * (i >> 2) + 4 * kh + (i & 3);
+            if (r < rows) brow[n0 + r] = static_cast<uint16_t>(float_to_bf16_rne(acc[wt][i] - accm[wt][i]));
+          }
       } else {
+        float* yrow = a.y + roff;
 #pragma unroll
         for (int wt = 0; wt < 2; ++wt)
 #pragma unroll
@@ -505,6 +517,7 @@ hipError_t launch_mmq(const MmqArgs& args, hipStream_t stream) {
   MmqArgs a = args;
   const int K = a.k / kQK;
   if (a.q_out && (!a.w_up || !a.d_out || a.partials || a.n % 64)) return hipErrorInvalidValue;
+  if (a.y_bf16 && (a.w_up || a.partials || a.splits > 1)) return hipErrorInvalidValue;
   if (a.splits <= 1 || a.w_up || a.partials) {
     a.splits = 1;
     a.split_blocks = K;

@@ -30,6 +30,12 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }
 
+// bfloat16 bits of a finite binary32 value, rounded to nearest even
+__device__ __forceinline__ uint32_t float_to_bf16_rne(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
 // 6-bit scale and min of sub-block s (0..7) from the header words.
 // Sub-blocks 0-3: scale = low 6 bits of scales[s], min = low 6 bits of
 // scales[s+4].  Sub-blocks 4-7: low 4 bits from scales[s+4] (scale: low

@@ -57,6 +57,9 @@ struct MmqArgs {
   const int8_t* qs;      // Q8_1 quants [m][k]
   const uint32_t* ds;    // Q8_1 scale/sum words [m][k/32]
   float* y;              // [m][n] f32 (h = silu(g) * u when w_up is set)
+  // single-matrix pass without k split: when set, y is not written and the
+  // result goes here as bfloat16 (rounded to nearest even) instead
+  uint16_t* y_bf16;
   // fused gate/up pass only (n % 64 == 0): h is quantised to Q8_1 in the
   // epilogue into q_out [m][n] and d_out [m][n/32] instead of stored to y
   int8_t* q_out;

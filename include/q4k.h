@@ -151,6 +151,14 @@ int q8_1_quantize(const void* x, int x_dtype, int m, int k, int8_t* qs, uint32_t
 int q4k_mmq(const void* w, const int8_t* qs, const uint32_t* ds, float* y, int m, int n,
             int k, void* stream);
 
+/* The same product with the result stored as bfloat16 from the tile
+   epilogue ("q4k_mmq.rs" header: the MMQ writes bf16 itself, no separate
+   cast): y[t][j] = bf16 rounding (to nearest even) of the value q4k_mmq
+   stores as f32, bit for bit.  y: device uint16 (bfloat16 bits) [m][n],
+   2-byte aligned, overwritten.  Same shape rules and errors as q4k_mmq. */
+int q4k_mmq_bf16(const void* w, const int8_t* qs, const uint32_t* ds, uint16_t* y, int m, int n,
+                 int k, void* stream);
+
 /* Q8_1-activation decode GEMV ("ffn.rs", fused_ffn_swiglu_gpu_true_dp4a:
    Q8_1 activations, integer dot products with the Q4_K quants, scales
    applied afterwards): the q4k_mmq product for a decode step's few tokens,

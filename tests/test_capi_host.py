@@ -35,7 +35,7 @@ def test_exports_every_declared_function(lib):
     assert {"q4k_gemv", "q8_1_quantize", "q4k_mmq", "ffn_swiglu_q4k", "q4k_weight_bytes",
             "q4k_status_string", "ffn_swiglu_q4k_workspace_bytes",
             "q4k_test_mmq_partials", "q4k_q8_gemv", "q4k_quantize", "q6k_gemv",
-            "q6k_weight_bytes"} <= set(names)
+            "q6k_weight_bytes", "q4k_mmq_bf16"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -165,3 +165,12 @@ def test_q6k_sizes_and_validation(lib):
     assert g(P, P + 4, P, 10, 256, None) == 3      # x needs 16 bytes
     assert g(P, P, P + 2, 10, 256, None) == 3
     assert g(P, P, P, 1 << 30, 32768, None) == 4   # block count overflows
+
+
+def test_mmq_bf16_validation(lib):
+    f = lib.q4k_mmq_bf16
+    assert f(P, P, P, None, 4, 64, 256, None) == 1      # no output
+    assert f(None, P, P, P, 4, 64, 256, None) == 1
+    assert f(P, P, P, P + 1, 4, 64, 256, None) == 3     # bf16 output needs 2 bytes
+    assert f(P, P, P, P, 4, 64, 300, None) == 2         # k not a multiple of 256
+    assert f(P, P, P, P, 0, 64, 256, None) == 2

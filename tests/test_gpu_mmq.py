@@ -94,3 +94,34 @@ def test_mmq_max_k(lib):
     p = empty((m, n, k // 32), torch.int32)
     lib.q4k_test_mmq_partials(dev(w), dev(qs), m, n, k, p)
     assert np.array_equal(host(p).astype(np.int64), orc.mmq_partials(w, n, k, qs))
+
+
+def bf16_rne(y32):
+    """bfloat16 bits of finite f32 values, rounded to nearest even (numpy)."""
+    b = y32.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 256), (3, 300, 512), (130, 520, 1024), (257, 64, 768),
+                                   (512, 5120, 17408)])
+def test_mmq_bf16_store(lib, m, n, k):
+    # the bf16 store is the nearest-even rounding of the f32 result, bit for
+    # bit; against the oracle it is within half a bf16 unit plus the f32 bound
+    say(f"mmq bf16 store m={m} n={n} k={k}")
+    w = synth.random_q4k(synth.rng(84, 1, m + n + k), n, k)
+    x = synth.activations(84, m, k, outliers=True, sub=m + n)
+    qs, d16, s = orc.q8_1_quantize(x)
+    ds = orc.pack_ds(d16, s).view(np.int32)
+    wd, qd, dd = dev(w), dev(qs), dev(ds)
+    y32 = empty((m, n), torch.float32)
+    y16 = empty((m, n), torch.int16)
+    lib.q4k_mmq(wd, qd, dd, y32, m, n, k)
+    lib.q4k_mmq_bf16(wd, qd, dd, y16, m, n, k)
+    y32, y16 = host(y32), host(y16).view(np.uint16)
+    assert np.array_equal(y16, bf16_rne(y32))
+    tokens = [0, m - 1] if m * n * k > 1 << 28 else list(range(m))
+    ref = orc.mmq(w, n, k, qs[tokens], d16[tokens], s[tokens])
+    got = synth.bf16_bits_to_f32(y16[tokens]).astype(np.float64)
+    bound = np.abs(ref) * 2.0 ** -8 + 1e-5 * orc.row_norms(w, n, k)[None, :] * \
+        np.linalg.norm(orc.q8_1_dequantize(qs[tokens], d16[tokens]), axis=1)[:, None]
+    assert np.all(np.abs(got - ref) <= bound)
