@@ -212,7 +212,7 @@ int q4k_quantize(const void* x, int x_dtype, int rows, int cols, void* w, void* 
   int st = check_matrix(rows, cols, &wbytes);
   if (st) return st;
   if ((st = check_elems(rows, cols))) return st;
-  if (!aligned(x, x_dtype == Q4K_F32 ? 16 : 8) || !aligned(w, kAlign)) return Q4K_ERR_ALIGN;
+  if (!aligned(x, kAlign) || !aligned(w, kAlign)) return Q4K_ERR_ALIGN;  // 16-byte loads of x
   if ((st = check_device())) return st;
   return launch_status(launch_quantize_q4k(x, x_dtype == Q4K_BF16, rows, cols, static_cast<uint8_t*>(w),
                                            static_cast<hipStream_t>(stream)));

@@ -118,8 +118,9 @@ int q4k_gemv(const void* w, const float* x, float* y, int m, int n, int k, void*
      the divisor is 0)
      q = rint((x + dmin*m_j) / (d*sc_j)), clamped to 0..15 (0 when d*sc_j = 0)
    Bit-exact by construction (IEEE operations only).  x: device [rows][cols]
-   of x_dtype (Q4K_F32, or Q4K_BF16 widened exactly); w: device block_q4_K
-   [rows][cols/256] (q4k_weight_bytes(rows, cols) bytes), overwritten.
+   of x_dtype (Q4K_F32, or Q4K_BF16 widened exactly), 16-byte aligned;
+   w: device block_q4_K [rows][cols/256] (q4k_weight_bytes(rows, cols)
+   bytes), 16-byte aligned, overwritten.
    rows >= 1, cols >= 256, cols % 256 == 0.  Inputs must be finite
    (non-finite input gives undefined codes but never faults).
    Errors: Q4K_ERR_NULL, Q4K_ERR_SHAPE, Q4K_ERR_ALIGN, Q4K_ERR_OVERFLOW,

@@ -96,7 +96,8 @@ def test_quantize_validation(lib):
     assert lib.q4k_quantize(P, 0, 0, 256, P, None) == 2
     assert lib.q4k_quantize(P, 0, 1, 300, P, None) == 2          # cols not a multiple of 256
     assert lib.q4k_quantize(P + 4, 0, 1, 256, P, None) == 3      # f32 input needs 16 bytes
-    assert lib.q4k_quantize(P + 8, 1, 1, 256, P + 4, None) == 3  # misaligned output
+    assert lib.q4k_quantize(P + 8, 1, 1, 256, P, None) == 3      # bf16 input needs 16 bytes too
+    assert lib.q4k_quantize(P, 1, 1, 256, P + 4, None) == 3      # misaligned output
     assert lib.q4k_quantize(P, 0, 1 << 30, 32768, P, None) == 4  # block count overflows
 
 

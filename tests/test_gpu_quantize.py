@@ -25,7 +25,7 @@ def test_quantize_bit_exact(lib, rows, cols, outliers):
     assert np.array_equal(quantize_gpu(lib, x, rows, cols), orc.q4k_quantize(x))
 
 
-@pytest.mark.parametrize("rows,cols", [(5, 512), (64, 2048)])
+@pytest.mark.parametrize("rows,cols", [(5, 512), (64, 2048), (3, 768), (1, 256)])
 def test_quantize_bf16_bit_exact(lib, rows, cols):
     say(f"q4k quantize bf16 rows={rows} cols={cols}")
     x = synth.bf16_bits_to_f32(synth.to_bf16_bits(synth.activations(99, rows, cols, outliers=True)))
