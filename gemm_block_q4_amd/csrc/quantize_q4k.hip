@@ -12,15 +12,14 @@
 // operation is an IEEE binary32 operation (min, max, subtract, correctly
 // rounded divide, rint, exact products), so the bytes are reproducible.
 //
-// Two blocks per wavefront, one per half-wave: lane l of a half holds values
-// 8l .. 8l+7 of its block (sub-block l/4).  Sub-block extrema take two
-// register-level lane exchanges among its 4 lanes (DPP) and the block maxima
-// three more within the half (DPP and the gfx950 row swap), so no exchange
-// goes through the LDS or crosses into the other block; lane l with l % 8 < 4
-// packs its eight quants with the eight of lane l + 4 (the high nibbles of
-// the same bytes) into 8 bytes of the quant field, and lanes 0 and 32 write
-// the headers.  The correctly rounded divisions make the kernel bound by its
-// vector-ALU work (about 130 instructions per block), not by the bytes it
+// Four blocks per wavefront, one per 16-lane row: lane l of a row holds
+// values 16l .. 16l+15 of its block (sub-block l/2).  Sub-block extrema take
+// one register-level lane exchange (DPP) and the block maxima three more, all
+// within the row, so no exchange goes through the LDS or crosses into another
+// block; lane l with l % 4 < 2 packs its sixteen quants with the sixteen of
+// lane l + 2 (the high nibbles of the same bytes) into 16 bytes of the quant
+// field, and lanes 0, 16, 32 and 48 write the headers.  The correctly rounded
+// divisions make the kernel bound by its vector-ALU work, not by the bytes it
 // reads (4 or 2 per value) and writes (0.5625 per value).
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
@@ -29,7 +28,7 @@ namespace q4k {
 
 namespace {
 
-constexpr int kQzThreads = 256;  // eight blocks per workgroup, two per wavefront
+constexpr int kQzThreads = 256;  // sixteen blocks per workgroup, four per wavefront
 
 // DPP move of v (row_mask all rows); lanes outside BANKS (4-lane groups of a
 // 16-lane row) keep old
@@ -49,15 +48,8 @@ __device__ __forceinline__ float lane_xor4(float v) {
 }
 __device__ __forceinline__ float lane_xor8(float v) { return dpp_move<0x128, 0xF>(v, v); }  // row_ror:8
 
-// maximum of v over lanes l and l ^ 16 (within each half-wave): a row swap
-// of two copies puts the partner's value beside the lane's own
-__device__ __forceinline__ float max_xor16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ uint32_t lane_xor4_u(uint32_t v) {
-  return __float_as_uint(lane_xor4(__uint_as_float(v)));
+__device__ __forceinline__ uint32_t lane_xor2_u(uint32_t v) {
+  return __float_as_uint(lane_xor2(__uint_as_float(v)));
 }
 
 // binary16 bits of v >= 0 (nearest even), 65504 where the rounding would overflow
@@ -70,55 +62,56 @@ __global__ __launch_bounds__(kQzThreads) void quantize_q4k_kernel(const void* __
                                                                   uint8_t* __restrict__ w,
                                                                   long long nblocks) {
   const int lane = threadIdx.x & 63;
-  const int hl = lane & 31;  // lane within the block's half-wave
-  const long long blk = (static_cast<long long>(blockIdx.x) * (kQzThreads / 64) + (threadIdx.x >> 6)) * 2 +
-                        (lane >> 5);
-  const bool valid = blk < nblocks;  // a missing second block reads block 0 and stores nothing
+  const int rl = lane & 15;  // lane within the block's row
+  const long long blk = (static_cast<long long>(blockIdx.x) * (kQzThreads / 64) + (threadIdx.x >> 6)) * 4 +
+                        (lane >> 4);
+  const bool valid = blk < nblocks;  // a missing block reads block 0 and stores nothing
   // rows are contiguous and a whole number of blocks long, so block blk holds
   // values 256 blk .. 256 blk + 255 of the matrix
-  const size_t e = static_cast<size_t>(valid ? blk : 0) * kQK + 8 * hl;
-  float v[8];
+  const size_t e = static_cast<size_t>(valid ? blk : 0) * kQK + 16 * rl;
+  float v[16];
   if constexpr (BF16) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + e);
-    const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_bits_to_float(r4[i] & 0xFFFFu);
-      v[2 * i + 1] = bf16_bits_to_float(r4[i] >> 16);
+    for (int c = 0; c < 2; ++c) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + e + 8 * c);
+      const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * c + 2 * i] = bf16_bits_to_float(r4[i] & 0xFFFFu);
+        v[8 * c + 2 * i + 1] = bf16_bits_to_float(r4[i] >> 16);
+      }
     }
   } else {
-    const float4 f0 = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + e);
-    const float4 f1 = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + e + 4);
-    v[0] = f0.x;
-    v[1] = f0.y;
-    v[2] = f0.z;
-    v[3] = f0.w;
-    v[4] = f1.x;
-    v[5] = f1.y;
-    v[6] = f1.z;
-    v[7] = f1.w;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(x) + e + 4 * c);
+      v[4 * c] = f.x;
+      v[4 * c + 1] = f.y;
+      v[4 * c + 2] = f.z;
+      v[4 * c + 3] = f.w;
+    }
   }
 
-  // sub-block extrema over its 4 lanes, then the step and offset
+  // sub-block extrema over its 2 lanes, then the step and offset
   float mn = v[0], mx = v[0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) {
+  for (int i = 1; i < 16; ++i) {
     mn = fminf(mn, v[i]);
     mx = fmaxf(mx, v[i]);
   }
   mn = fminf(mn, lane_xor1(mn));
   mx = fmaxf(mx, lane_xor1(mx));
-  mn = fminf(mn, lane_xor2(mn));
-  mx = fmaxf(mx, lane_xor2(mx));
   const float lo = fminf(mn, 0.0f);
   const float o = 0.0f - lo;
   const float s = mx > lo ? (mx - lo) / 15.0f : 0.0f;
 
-  // block scale and min: maxima over the 8 sub-blocks (lanes l ^ 4, ^ 8, ^ 16)
-  float smax = fmaxf(s, lane_xor4(s));
-  float omax = fmaxf(o, lane_xor4(o));
-  smax = max_xor16(fmaxf(smax, lane_xor8(smax)));
-  omax = max_xor16(fmaxf(omax, lane_xor8(omax)));
+  // block scale and min: maxima over the 8 sub-blocks (lanes l ^ 2, ^ 4, ^ 8)
+  float smax = fmaxf(s, lane_xor2(s));
+  float omax = fmaxf(o, lane_xor2(o));
+  smax = fmaxf(smax, lane_xor4(smax));
+  omax = fmaxf(omax, lane_xor4(omax));
+  smax = fmaxf(smax, lane_xor8(smax));
+  omax = fmaxf(omax, lane_xor8(omax));
   const uint32_t dbits = f16_bits_saturating(smax / 63.0f);
   const uint32_t mbits = f16_bits_saturating(omax / 63.0f);
   const float d = half_bits_to_float(dbits);
@@ -128,46 +121,55 @@ __global__ __launch_bounds__(kQzThreads) void quantize_q4k_kernel(const void* __
   const float ds = d * static_cast<float>(sc);    // exact: 11 x 6 bits
   const float dm = dmin * static_cast<float>(mm);
 
-  // quants: value 8l + i of the block is nibble (l % 8 < 4 ? low : high) of
-  // quant byte 32 (l / 8) + 8 (l % 4) + i
-  uint32_t q4[2] = {0u, 0u};
+  // quants: value 16l + i of the block is nibble (l % 4 < 2 ? low : high) of
+  // quant byte 32 (l / 4) + 16 (l % 2) + i
+  uint32_t q4[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 16; ++i) {
     const uint32_t q = ds > 0.0f ? static_cast<uint32_t>(fminf(fmaxf(rintf((v[i] + dm) / ds), 0.0f), 15.0f)) : 0u;
     q4[i >> 2] |= q << (8 * (i & 3));
   }
-  const uint32_t hi0 = lane_xor4_u(q4[0]), hi1 = lane_xor4_u(q4[1]);
+  uint32_t hi[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) hi[c] = lane_xor2_u(q4[c]);
   uint8_t* out = w + static_cast<size_t>(valid ? blk : 0) * kBlockBytes;
-  if (valid && (hl & 4) == 0)
-    *reinterpret_cast<uint2*>(out + 16 + 32 * (hl >> 3) + 8 * (hl & 3)) =
-        make_uint2(q4[0] | (hi0 << 4), q4[1] | (hi1 << 4));
+  if (valid && (rl & 2) == 0)
+    *reinterpret_cast<uint4*>(out + 16 + 32 * (rl >> 2) + 16 * (rl & 1)) =
+        make_uint4(q4[0] | (hi[0] << 4), q4[1] | (hi[1] << 4), q4[2] | (hi[2] << 4), q4[3] | (hi[3] << 4));
 
   // headers: d, dmin and the eight 6-bit pairs of each block (sub-block j's
-  // in lane 4j of the block's half)
-  uint32_t hw[2][3];
+  // in lane 2j of the block's row)
+  uint32_t hw[4][3];
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
+  for (int row = 0; row < 4; ++row) {
     uint32_t scj[8], mj[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      scj[j] = static_cast<uint32_t>(__builtin_amdgcn_readlane(sc, 32 * half + 4 * j));
-      mj[j] = static_cast<uint32_t>(__builtin_amdgcn_readlane(mm, 32 * half + 4 * j));
+      scj[j] = static_cast<uint32_t>(__builtin_amdgcn_readlane(sc, 16 * row + 2 * j));
+      mj[j] = static_cast<uint32_t>(__builtin_amdgcn_readlane(mm, 16 * row + 2 * j));
     }
-    hw[half][0] = hw[half][1] = hw[half][2] = 0u;
+    hw[row][0] = hw[row][1] = hw[row][2] = 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t b0 = (scj[j] & 63u) | ((scj[j + 4] >> 4) << 6);
       const uint32_t b1 = (mj[j] & 63u) | ((mj[j + 4] >> 4) << 6);
       const uint32_t b2 = (scj[j + 4] & 15u) | ((mj[j + 4] & 15u) << 4);
-      hw[half][0] |= b0 << (8 * j);
-      hw[half][1] |= b1 << (8 * j);
-      hw[half][2] |= b2 << (8 * j);
+      hw[row][0] |= b0 << (8 * j);
+      hw[row][1] |= b1 << (8 * j);
+      hw[row][2] |= b2 << (8 * j);
     }
   }
-  if (valid && hl == 0) {
-    const bool second = lane >= 32;
-    *reinterpret_cast<uint4*>(out) = make_uint4(dbits | (mbits << 16), second ? hw[1][0] : hw[0][0],
-                                                second ? hw[1][1] : hw[0][1], second ? hw[1][2] : hw[0][2]);
+  if (valid && rl == 0) {
+    const int row = lane >> 4;
+    uint32_t h0 = hw[0][0], h1 = hw[0][1], h2 = hw[0][2];
+#pragma unroll
+    for (int r = 1; r < 4; ++r)
+      if (row == r) {
+        h0 = hw[r][0];
+        h1 = hw[r][1];
+        h2 = hw[r][2];
+      }
+    *reinterpret_cast<uint4*>(out) = make_uint4(dbits | (mbits << 16), h0, h1, h2);
   }
 }
 
@@ -177,7 +179,7 @@ hipError_t launch_quantize_q4k(const void* x, int x_bf16, int rows, int cols, ui
                                hipStream_t stream) {
   if (rows < 1 || cols < kQK || cols % kQK) return hipErrorInvalidValue;
   const long long nblocks = static_cast<long long>(rows) * (cols / kQK);
-  constexpr int per_group = 2 * (kQzThreads / 64);
+  constexpr int per_group = 4 * (kQzThreads / 64);
   const long long groups = (nblocks + per_group - 1) / per_group;
   if (groups > 0x7FFFFFFFLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(groups));
