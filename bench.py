@@ -43,7 +43,7 @@ TRAFFIC_SOURCES = {
     "gemm_block_q4_amd/csrc/gemv_valu.hip":
         "094eb220de80c4311a76906daa74afab5fc87a363c377b585b77aa182bab1b42",
     "gemm_block_q4_amd/csrc/q4k_device.hpp":
-        "0ca9cfd803b914df0ad564490c5fd4e9deb5aaf1f4e89c866e6dd71f630d251d",
+        "532c6e881bd56ddab7a0e075b479fbab8468380451639a48865dc41a8cb9352e",
 }
 
 
