@@ -63,3 +63,46 @@ def test_quantize_then_gemv_matches_dequantised_weights(lib):
     err = orc.normalized_max_error(host(y), ref, orc.row_norms(w, rows, cols),
                                    np.linalg.norm(a.astype(np.float64), axis=1))
     assert err <= 1e-5, err
+
+
+def tie_inputs(rows, cols, seed):
+    """Weights at the half-integer points of their own block grid.
+
+    Each 32-value sub-block gets its minimum -L_j (0 for half of them) at
+    position 0 and its maximum 15 S - L_j at position 1, with one step S per
+    block, so the oracle's fit gives every sub-block the same scale code and
+    the quantiser keeps that fit however the other 30 values move inside
+    [-L_j, 15 S - L_j].  Those are then set to binary32 (k + 1/2) ds - dm for
+    the block's stored ds = d sc_j and dm = dmin m_j: (x + dm) / ds is at or
+    within a few units of the last place of k + 1/2, where the rounding of
+    the quotient and then to an integer decides the code."""
+    rng = np.random.default_rng(seed)
+    nb = cols // 256
+    x = np.zeros((rows, nb, 8, 32), dtype=np.float32)
+    S = rng.uniform(0.01, 2.0, (rows, nb, 1)).astype(np.float32)
+    L = np.where(rng.random((rows, nb, 8)) < 0.5, 0.0, rng.uniform(0.1, 5.0, (rows, nb, 8))).astype(np.float32)
+    x[..., 0] = -L
+    x[..., 1] = (np.float32(15.0) * S - L).astype(np.float32)
+    x[..., 2:] = (rng.uniform(0, 15, (rows, nb, 8, 30)) * S[..., None] - L[..., None]).astype(np.float32)
+    x = x.reshape(rows, cols)
+    d, dmin, sc, mn, _ = orc.block_fields(orc.q4k_quantize(x), rows, cols)
+    ds = (d.astype(np.float32)[..., None] * sc.astype(np.float32)).astype(np.float32)
+    dm = (dmin.astype(np.float32)[..., None] * mn.astype(np.float32)).astype(np.float32)
+    k = rng.integers(0, 15, (rows, nb, 8, 30)).astype(np.float32)
+    xb = x.reshape(rows, nb, 8, 32)
+    xb[..., 2:] = ((k + np.float32(0.5)) * ds[..., None] - dm[..., None]).astype(np.float32)
+    xb[..., 2:] = np.clip(xb[..., 2:], xb[..., :1], xb[..., 1:2])  # stay inside the fitted range
+    out = xb.reshape(rows, cols)
+    # the fit is unchanged by the move
+    assert np.array_equal(orc.block_fields(orc.q4k_quantize(out), rows, cols)[2], sc)
+    return out
+
+
+@pytest.mark.parametrize("rows,cols", [(64, 1024), (37, 2304)])
+def test_quantize_grid_midpoints_bit_exact(lib, rows, cols):
+    # quotients at or next to k + 1/2: the rounding of the division and then
+    # to an integer (ties to even) must match the oracle's binary32 steps
+    say(f"q4k quantize grid midpoints rows={rows} cols={cols}")
+    x = tie_inputs(rows, cols, 103 + rows)
+    ref = orc.q4k_quantize(x)
+    assert np.array_equal(quantize_gpu(lib, x, rows, cols), ref)
