@@ -18,9 +18,10 @@
 // within the row, so no exchange goes through the LDS or crosses into another
 // block; lane l with l % 4 < 2 packs its sixteen quants with the sixteen of
 // lane l + 2 (the high nibbles of the same bytes) into 16 bytes of the quant
-// field, and lanes 0, 16, 32 and 48 write the headers.  The correctly rounded
-// divisions make the kernel bound by its vector-ALU work, not by the bytes it
-// reads (4 or 2 per value) and writes (0.5625 per value).
+// field, and lanes 0, 16, 32 and 48 write the headers.  Its vector-ALU work
+// (the per-sub-block divisions, the codes, the header gathering) and latency
+// bound it rather than the bytes it reads (4 or 2 per value) and writes
+// (0.5625 per value).
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
 
