@@ -70,3 +70,18 @@ def test_q8_1_large_intermediate(lib):
     g = np.random.default_rng(5)
     x = (g.standard_normal((64, 17408)) * g.choice([1.0, 1e3, 1e5], (64, 17408))).astype(np.float32)
     check(lib, x, False)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_q8_1_exact_ties(lib, bf16):
+    # amax = 127 * 2^e, so d = 2^e exactly, and the other values (j + 1/2) 2^e:
+    # every quotient is exactly a half-integer and rounds to even (all values
+    # have at most 8 significant bits, so bf16 holds them too)
+    say(f"q8_1 exact ties bf16={bf16}")
+    rng = np.random.default_rng(7)
+    m, k = 64, 1024
+    e = rng.integers(-10, 10, (m, k // 32, 1)).astype(np.float64)
+    j = rng.integers(-126, 126, (m, k // 32, 32)).astype(np.float64)
+    x = (j + 0.5) * 2.0 ** e
+    x[..., 0] = 127.0 * 2.0 ** e[..., 0]
+    check(lib, x.reshape(m, k).astype(np.float32), bf16)
