@@ -106,3 +106,14 @@ def test_quantize_grid_midpoints_bit_exact(lib, rows, cols):
     x = tie_inputs(rows, cols, 103 + rows)
     ref = orc.q4k_quantize(x)
     assert np.array_equal(quantize_gpu(lib, x, rows, cols), ref)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_quantize_full_size_bit_exact(lib, bf16):
+    # the [11008, 4096] matrix bench.py times, every byte against the oracle
+    rows, cols = 11008, 4096
+    say(f"q4k quantize full size {rows}x{cols} bf16={bf16}")
+    x = synth.activations(synth.GEMV_SWEEP, rows, cols, False, sub=200)
+    if bf16:
+        x = synth.bf16_bits_to_f32(synth.to_bf16_bits(x))
+    assert np.array_equal(quantize_gpu(lib, x, rows, cols, bf16=bf16), orc.q4k_quantize(x))
