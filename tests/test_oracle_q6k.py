@@ -123,3 +123,59 @@ def test_sizes_and_rejects():
             pass
         else:
             raise AssertionError(bad)
+
+
+def _decode_with(unpack, block):
+    """The oracle's dequantisation with another 6-bit unpacker (mutation check)."""
+    u = unpack(block[0:128][None], block[128:192][None])[0].astype(np.float64) - 32.0
+    sc = block[192:208].view(np.int8).astype(np.float64)
+    d = float(np.array([int(block[208]) | (int(block[209]) << 8)], dtype=np.uint16).view(np.float16)[0])
+    return d * np.repeat(sc, 16) * u
+
+
+def test_hand_block_catches_planted_layout_mistakes():
+    # each plausible misreading of the layout, planted in a copy of the
+    # unpacker, changes at least one hand-derived weight
+    h, block = hand_block()
+    want = {int(k): v for k, v in h["weights"].items()}
+
+    def swapped_nibbles(ql, qh):      # high nibble for quarters 0-1
+        out = q6.unpack_q6(ql, qh).copy()
+        for hh in range(2):
+            for r in range(4):
+                src = ql[..., 64 * hh + 32 * (r % 2): 64 * hh + 32 * (r % 2) + 32]
+                low = (src & 0x0F) if r >= 2 else (src >> 4)
+                out[..., 128 * hh + 32 * r: 128 * hh + 32 * r + 32] = (out[..., 128 * hh + 32 * r: 128 * hh + 32 * r + 32] & 0x30) | low
+        return out
+
+    def reversed_high_bits(ql, qh):   # quarter r takes bits 6-2r, 7-2r
+        out = q6.unpack_q6(ql, qh).copy()
+        for hh in range(2):
+            for r in range(4):
+                hi = (qh[..., 32 * hh: 32 * hh + 32] >> (6 - 2 * r)) & 3
+                sl = slice(128 * hh + 32 * r, 128 * hh + 32 * r + 32)
+                out[..., sl] = (out[..., sl] & 0x0F) | (hi << 4)
+        return out
+
+    def ql_quarters_swapped(ql, qh):  # quarter r reads ql[64h + 32(r // 2) + l]
+        out = q6.unpack_q6(ql, qh).copy()
+        for hh in range(2):
+            for r in range(4):
+                src = ql[..., 64 * hh + 32 * (r // 2): 64 * hh + 32 * (r // 2) + 32]
+                low = (src >> 4) if r >= 2 else (src & 0x0F)
+                sl = slice(128 * hh + 32 * r, 128 * hh + 32 * r + 32)
+                out[..., sl] = (out[..., sl] & 0x30) | low
+        return out
+
+    assert all(_decode_with(q6.unpack_q6, block)[i] == v for i, v in want.items())
+    for mutant in (swapped_nibbles, reversed_high_bits, ql_quarters_swapped):
+        w = _decode_with(mutant, block)
+        assert any(w[i] != v for i, v in want.items()), mutant.__name__
+    # a scale per 32 weights instead of 16, and no -32 offset
+    w = q6.dequantize(block, 1, 256)[0]
+    u = q6.unpack_q6(block[0:128][None], block[128:192][None])[0].astype(np.float64)
+    per32 = 0.5 * np.repeat(block[192:208].view(np.int8)[:8].astype(np.float64), 32) * (u - 32)
+    no_offset = 0.5 * np.repeat(block[192:208].view(np.int8).astype(np.float64), 16) * u
+    assert any(per32[i] != v for i, v in want.items())
+    assert any(no_offset[i] != v for i, v in want.items())
+    assert all(w[i] == v for i, v in want.items())
