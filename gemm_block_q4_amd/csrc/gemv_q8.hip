@@ -326,7 +326,7 @@ Q8Geo make_q8_geo(int n, int k) {
 template <int MT, bool GU>
 hipError_t launch_mt(const uint8_t* w, const uint8_t* wu, const int8_t* qs, const uint32_t* ds, float* y,
                      int m, int n, int k, hipStream_t stream) {
-  constexpr int PF = (MT >= 8 ? 2 : 4) / (GU ? 2 : 1);
+  constexpr int PF = GU && MT == 1 ? 4 : (MT >= 8 ? 2 : 4) / (GU ? 2 : 1);
   constexpr int NM = GU ? 2 : 1;
   const Q8Geo g = make_q8_geo(n, k);
   const size_t lds = g.wr > 1 ? static_cast<size_t>(g.rpg) * g.wr * NM * MT * sizeof(float) : 0;
