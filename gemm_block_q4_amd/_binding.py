@@ -1,8 +1,10 @@
 """ctypes binding of ``libq4k.so`` (the C ABI in ``include/q4k.h``).
 
-Argument marshalling only: torch tensors are checked for device, dtype and
-contiguity, then their device pointers and the current HIP stream are handed
-to the library.  Every computation runs in the library's HIP kernels; there is
+Argument marshalling only: every torch tensor is checked for dtype, for
+holding at least the bytes the call will touch, for contiguity and for living
+on the GPU (``ValueError`` otherwise), then its device pointer and the current
+HIP stream are handed to the library, which validates shapes, alignment and
+sizes again on the host.  Every computation runs in the library's HIP kernels; there is
 no fallback, and a missing library raises :class:`Q4KError`.
 """
 
@@ -73,14 +75,45 @@ def _check(status: int) -> None:
         raise Q4KError(status, msg)
 
 
-def _ptr(t) -> int | None:
-    if t is None:
-        return None
-    if not t.is_cuda:
-        raise ValueError("tensor must live on the GPU")
-    if not t.is_contiguous():
-        raise ValueError("tensor must be contiguous")
-    return t.data_ptr()
+# dtype names accepted for each kind of buffer (torch dtype names)
+_BYTES = ("uint8", "int8")
+_F32 = ("float32",)
+_BF16 = ("int16", "uint16", "bfloat16")
+_I32 = ("int32", "uint32")
+
+
+def _ptrs(*specs) -> list:
+    """Device pointers of the tensors in ``specs``, each ``(tensor, nbytes,
+    dtypes, name)``: every tensor is first checked for an accepted dtype (None:
+    any), for holding at least ``nbytes`` bytes and for contiguity, then every
+    tensor for living on the GPU.  ``None`` passes through (the library reports
+    a missing pointer)."""
+    for t, nbytes, dtypes, name in specs:
+        if t is None:
+            continue
+        if dtypes is not None and str(t.dtype).replace("torch.", "") not in dtypes:
+            raise ValueError(f"{name}: dtype {t.dtype} not one of {', '.join(dtypes)}")
+        have = t.numel() * t.element_size()
+        if have < nbytes:
+            raise ValueError(f"{name}: holds {have} bytes, the call needs {nbytes}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: tensor must be contiguous")
+    for t, _, _, name in specs:
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name}: tensor must live on the GPU")
+    return [None if t is None else t.data_ptr() for t, _, _, _ in specs]
+
+
+def _pos(*v: int) -> bool:
+    return all(int(a) > 0 for a in v)
+
+
+def _x_dtypes(x_dtype: int):
+    return _BF16 if x_dtype == Q4K_BF16 else _F32
+
+
+def _x_size(x_dtype: int) -> int:
+    return 2 if x_dtype == Q4K_BF16 else 4
 
 
 def _stream(stream) -> int:
@@ -106,54 +139,89 @@ def ffn_swiglu_q4k_workspace_bytes(m: int, hidden: int, inter: int, top_k: int =
 
 
 # -- device entry points --------------------------------------------------------
+# (sizes are only computed for positive shapes; the library rejects the rest)
+
+def _q8_specs(w, qs, ds, m: int, n: int, k: int, ok: bool):
+    """Checks of a Q4_K matrix [n, k] and the Q8_1 activations [m, k]."""
+    return ((w, q4k_weight_bytes(n, k) if ok else 0, _BYTES, "w"),
+            (qs, m * k if ok else 0, _BYTES, "qs"),
+            (ds, 4 * m * (k // 32) if ok else 0, _I32, "ds"))
+
 
 def q4k_gemv(w, x, y, m: int, n: int, k: int, stream=None) -> None:
     """y[m, n] = x[m, k] @ dequant(w)[n, k]^T on the GPU (``q4k_gemv``)."""
-    _check(load_library().q4k_gemv(_ptr(w), _ptr(x), _ptr(y), m, n, k, _stream(stream)))
+    ok = _pos(m, n, k)
+    pw, px, py = _ptrs((w, q4k_weight_bytes(n, k) if ok else 0, _BYTES, "w"),
+                       (x, 4 * m * k if ok else 0, _F32, "x"),
+                       (y, 4 * m * n if ok else 0, _F32, "y"))
+    _check(load_library().q4k_gemv(pw, px, py, m, n, k, _stream(stream)))
 
 
 def q8_1_quantize(x, x_dtype: int, m: int, k: int, qs, ds, stream=None) -> None:
-    _check(load_library().q8_1_quantize(_ptr(x), x_dtype, m, k, _ptr(qs), _ptr(ds),
-                                        _stream(stream)))
+    ok = _pos(m, k)
+    px, pq, pd = _ptrs((x, _x_size(x_dtype) * m * k if ok else 0, _x_dtypes(x_dtype), "x"),
+                       (qs, m * k if ok else 0, _BYTES, "qs"),
+                       (ds, 4 * m * (k // 32) if ok else 0, _I32, "ds"))
+    _check(load_library().q8_1_quantize(px, x_dtype, m, k, pq, pd, _stream(stream)))
 
 
 def q4k_mmq(w, qs, ds, y, m: int, n: int, k: int, stream=None) -> None:
-    _check(load_library().q4k_mmq(_ptr(w), _ptr(qs), _ptr(ds), _ptr(y), m, n, k,
-                                  _stream(stream)))
+    ok = _pos(m, n, k)
+    p = _ptrs(*_q8_specs(w, qs, ds, m, n, k, ok), (y, 4 * m * n if ok else 0, _F32, "y"))
+    _check(load_library().q4k_mmq(*p, m, n, k, _stream(stream)))
 
 
 def q4k_mmq_bf16(w, qs, ds, y, m: int, n: int, k: int, stream=None) -> None:
     """q4k_mmq with the result stored as bfloat16 bits (y: int16 or uint16 [m, n])."""
-    _check(load_library().q4k_mmq_bf16(_ptr(w), _ptr(qs), _ptr(ds), _ptr(y), m, n, k,
-                                       _stream(stream)))
+    ok = _pos(m, n, k)
+    p = _ptrs(*_q8_specs(w, qs, ds, m, n, k, ok), (y, 2 * m * n if ok else 0, _BF16, "y"))
+    _check(load_library().q4k_mmq_bf16(*p, m, n, k, _stream(stream)))
 
 
 def q4k_quantize(x, x_dtype: int, rows: int, cols: int, w, stream=None) -> None:
     """Encode weights x [rows, cols] (f32 or bf16 bits) to block_q4_K bytes w."""
-    _check(load_library().q4k_quantize(_ptr(x), x_dtype, rows, cols, _ptr(w), _stream(stream)))
+    ok = _pos(rows, cols)
+    px, pw = _ptrs((x, _x_size(x_dtype) * rows * cols if ok else 0, _x_dtypes(x_dtype), "x"),
+                   (w, q4k_weight_bytes(rows, cols) if ok else 0, _BYTES, "w"))
+    _check(load_library().q4k_quantize(px, x_dtype, rows, cols, pw, _stream(stream)))
 
 
 def q4k_q8_gemv(w, qs, ds, y, m: int, n: int, k: int, stream=None) -> None:
     """y[m, n] = reference dot of Q8_1 rows (qs, ds) with the Q4_K rows, m <= 8."""
-    _check(load_library().q4k_q8_gemv(_ptr(w), _ptr(qs), _ptr(ds), _ptr(y), m, n, k,
-                                      _stream(stream)))
+    ok = _pos(m, n, k)
+    p = _ptrs(*_q8_specs(w, qs, ds, m, n, k, ok), (y, 4 * m * n if ok else 0, _F32, "y"))
+    _check(load_library().q4k_q8_gemv(*p, m, n, k, _stream(stream)))
 
 
 def q6k_gemv(w, x, y, n: int, k: int, stream=None) -> None:
     """y[n] = dequant(w)[n, k] @ x[k] for Q6_K weights w (one f32 token)."""
-    _check(load_library().q6k_gemv(_ptr(w), _ptr(x), _ptr(y), n, k, _stream(stream)))
+    ok = _pos(n, k)
+    pw, px, py = _ptrs((w, q6k_weight_bytes(n, k) if ok else 0, _BYTES, "w"),
+                       (x, 4 * k if ok else 0, _F32, "x"),
+                       (y, 4 * n if ok else 0, _F32, "y"))
+    _check(load_library().q6k_gemv(pw, px, py, n, k, _stream(stream)))
 
 
 def q4k_test_mmq_partials(w, qs, m: int, n: int, k: int, partials, stream=None) -> None:
-    _check(load_library().q4k_test_mmq_partials(_ptr(w), _ptr(qs), m, n, k, _ptr(partials),
-                                                _stream(stream)))
+    ok = _pos(m, n, k)
+    pw, pq, pp = _ptrs((w, q4k_weight_bytes(n, k) if ok else 0, _BYTES, "w"),
+                       (qs, m * k if ok else 0, _BYTES, "qs"),
+                       (partials, 4 * m * n * (k // 32) if ok else 0, _I32, "partials"))
+    _check(load_library().q4k_test_mmq_partials(pw, pq, m, n, k, pp, _stream(stream)))
 
 
 def ffn_swiglu_q4k(w_gate, w_up, w_down, x, x_dtype: int, m: int, hidden: int, inter: int,
                    y, workspace, n_experts: int = 1, ids=None, wts=None, top_k: int = 0,
                    regime: int = Q4K_REGIME_AUTO, stream=None) -> None:
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(load_library().ffn_swiglu_q4k(
-        _ptr(w_gate), _ptr(w_up), _ptr(w_down), n_experts, _ptr(x), x_dtype, m, hidden, inter,
-        _ptr(ids), _ptr(wts), top_k, regime, _ptr(y), _ptr(workspace), ws_bytes,
-        _stream(stream)))
+    ok = _pos(m, hidden, inter, n_experts)
+    gu = n_experts * q4k_weight_bytes(inter, hidden) if ok else 0
+    dn = n_experts * q4k_weight_bytes(hidden, inter) if ok else 0
+    pairs = m * top_k if ok and ids is not None and top_k > 0 else 0
+    pg, pu, pd, px, pi, pt, py, pws = _ptrs(
+        (w_gate, gu, _BYTES, "w_gate"), (w_up, gu, _BYTES, "w_up"), (w_down, dn, _BYTES, "w_down"),
+        (x, _x_size(x_dtype) * m * hidden if ok else 0, _x_dtypes(x_dtype), "x"),
+        (ids, 4 * pairs, _I32, "ids"), (wts, 4 * pairs, _F32, "wts"),
+        (y, 4 * m * hidden if ok else 0, _F32, "y"), (workspace, 0, None, "workspace"))
+    _check(load_library().ffn_swiglu_q4k(pg, pu, pd, n_experts, px, x_dtype, m, hidden, inter, pi, pt,
+                                         top_k, regime, py, pws, ws_bytes, _stream(stream)))

@@ -9,10 +9,35 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
+#include <set>
+#include <utility>
 
 #include "../../include/q4k.h"
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
+
+namespace q4k {
+
+hipError_t lds_opt_in(const void* kern, size_t lds) {
+  constexpr size_t kDefaultLds = 64 * 1024;
+  constexpr size_t kLdsPerCu = 160 * 1024;
+  if (lds <= kDefaultLds) return hipSuccess;
+  if (lds > kLdsPerCu) return hipErrorInvalidValue;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::mutex mu;
+  static std::set<std::pair<const void*, int>> done;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({kern, dev})) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsPerCu));
+  if (e != hipSuccess) return e;
+  done.insert({kern, dev});
+  return hipSuccess;
+}
+
+}  // namespace q4k
 
 using namespace q4k;
 

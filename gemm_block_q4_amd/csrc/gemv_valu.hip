@@ -705,14 +705,8 @@ template <bool GU, bool BF16, int MODE, int LAYOUT, int XU>
 hipError_t launch_layout(const GemvArgs& a, const Geo& geo, size_t lds, int grid_y, hipStream_t stream) {
   constexpr int PF = GU ? 2 : 4;
   auto kern = gemv_d4_kernel<GU, BF16, MODE, LAYOUT, XU, PF>;
-  static bool big_lds = false;  // the opt-in is per kernel and stays set
-  if (lds > 64 * 1024 && !big_lds) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(kLdsMax));
-    if (e != hipSuccess) return e;
-    big_lds = true;
-  }
+  const hipError_t e = lds_opt_in(reinterpret_cast<const void*>(kern), lds);
+  if (e != hipSuccess) return e;
   const dim3 grid((a.n + geo.rows - 1) / geo.rows, grid_y);
   kern<<<grid, dim3(geo.waves * 64), lds, stream>>>(a, geo);
   return hipGetLastError();
@@ -778,14 +772,8 @@ hipError_t launch_moe_down(const GemvArgs& a, hipStream_t stream) {
   const int xu = (16 * K + 63) / 64;  // activation units per lane (1..4)
   const dim3 grid((a.n + g.rows - 1) / g.rows, a.m);
   auto go = [&](auto kern) -> hipError_t {
-    static bool big_lds = false;
-    if (lds > 64 * 1024 && !big_lds) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               static_cast<int>(kLdsMax));
-      if (e != hipSuccess) return e;
-      big_lds = true;
-    }
+    const hipError_t e = lds_opt_in(reinterpret_cast<const void*>(kern), lds);
+    if (e != hipSuccess) return e;
     kern<<<grid, dim3(g.waves * 64), lds, stream>>>(a, g);
     return hipGetLastError();
   };

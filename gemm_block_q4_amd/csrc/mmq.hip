@@ -499,14 +499,8 @@ hipError_t launch(const MmqArgs& a, hipStream_t stream) {
   const dim3 grid((a.n + RPM - 1) / RPM, (a.m + kBM - 1) / kBM, a.splits);
   const size_t lds = 2 * sizeof(Stage);
   auto kern = mmq_kernel<GU, PARTIALS>;
-  static bool big_lds = false;  // the opt-in is per kernel and stays set
-  if (!big_lds) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    big_lds = true;
-  }
+  const hipError_t e = lds_opt_in(reinterpret_cast<const void*>(kern), lds);
+  if (e != hipSuccess) return e;
   kern<<<grid, dim3(kThreads), lds, stream>>>(a);
   return hipGetLastError();
 }

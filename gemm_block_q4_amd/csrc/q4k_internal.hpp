@@ -9,6 +9,12 @@
 
 namespace q4k {
 
+// Lets `kern` use `lds` bytes of dynamic LDS on the current device: above the
+// default 64 KiB limit the kernel is opted in (hipFuncSetAttribute) once per
+// (kernel, device) pair; the registry of done pairs is guarded by a mutex, so
+// concurrent callers on any devices are safe.
+hipError_t lds_opt_in(const void* kern, size_t lds);
+
 // GEMV over one dense matrix, or one of the two MoE passes over expert banks
 // (expert e's matrix at e * mat_bytes).
 struct GemvArgs {

@@ -24,7 +24,7 @@
  *   - Pointers named as device pointers must point to device memory of the
  *     current HIP device; the caller owns every buffer and keeps it alive until
  *     the stream has run the call.  The library allocates nothing and keeps no
- *     state between calls.
+ *     data between calls (the per-device caches below aside).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Every call is
  *     asynchronous on it; nothing synchronises inside the library.
  *   - Arguments are validated on the host before any launch; on error nothing
@@ -33,7 +33,11 @@
  *   - Weight matrices, activations, quantised activations and the workspace
  *     must be 16-byte aligned (a 144-byte block is nine 16-byte words, so all
  *     blocks stay aligned).  Routing ids and weights need 4-byte alignment.
- *   - Calls are reentrant: no global state is written.
+ *   - Calls are reentrant and may come from several host threads at once.
+ *     The only process-wide state is a cache per device ordinal (whether it is
+ *     a gfx950, its compute-unit count: atomics) and the set of (kernel,
+ *     device) pairs already opted into more than 64 KiB of LDS (guarded by a
+ *     mutex); each is written once per device and never changes a result.
  *
  * block_q4_K (GGML layout): bytes 0-1 fp16 d, 2-3 fp16 dmin, 4-15 twelve
  * bytes of packed 6-bit (scale, min) pairs for eight 32-weight sub-blocks,

@@ -120,8 +120,17 @@ def prefill_weights():
     return synth.dense_ffn_weights(synth.PREFILL_FFN, 5120, 17408)
 
 
-@pytest.mark.parametrize("m,tokens", [(512, [0, 255, 511]), (2048, [1, 1024, 2047])])
-def test_prefill_ffn_full_size(lib, prefill_weights, m, tokens):
+def tile_sample(m, tile=128):
+    """One token from every tile of `tile` tokens (a different position in each
+    tile, so that different lanes and accumulator rows are compared) plus the
+    last token."""
+    tokens = [min(m - 1, tile * i + (37 * i + 5) % tile) for i in range((m + tile - 1) // tile)]
+    return sorted(set(tokens + [m - 1]))
+
+
+@pytest.mark.parametrize("m", [512, 2048])
+def test_prefill_ffn_full_size(lib, prefill_weights, m):
+    tokens = tile_sample(m)
     say(f"ffn prefill 5120/17408 m={m} (sampled tokens {tokens})")
     wg, wu, wd = prefill_weights
     x = synth.activations(synth.PREFILL_FFN, m, 5120, outliers=True, sub=m)

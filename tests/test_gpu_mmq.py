@@ -78,7 +78,10 @@ def test_mmq_prefill_gate_full_size(lib):
     say(f"mmq full size m={m} n={n} k={k} (sampled tokens)")
     w = synth.random_q4k(synth.rng(84, 1), n, k)
     qs, d16, s = quantised(m, k, 7, bf16=True)
-    y1 = check(lib, w, qs, d16, s, n, k, tokens=[0, 63, 64, 300, 511])
+    # one token from every 128-token tile (a different position in each) and
+    # the last one
+    tokens = sorted({128 * i + (37 * i + 5) % 128 for i in range(m // 128)} | {0, 63, 64, m - 1})
+    y1 = check(lib, w, qs, d16, s, n, k, tokens=tokens)
     y2 = mmq_gpu(lib, w, qs, d16, s, n, k)
     assert np.array_equal(y1, y2)
 
