@@ -13,8 +13,10 @@ from ._binding import (  # noqa: F401
     Q4K_REGIME_DECODE,
     Q4K_REGIME_PREFILL,
     Q4K_REGIME_DECODE_Q8,
+    Q4K_NOALLOC_SCRATCH_BYTES,
     Q4KError,
     ffn_swiglu_q4k,
+    ffn_swiglu_q4k_noalloc,
     ffn_swiglu_q4k_workspace_bytes,
     library_path,
     load_library,

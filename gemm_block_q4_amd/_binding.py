@@ -48,7 +48,12 @@ _SIGNATURES = {
     "ffn_swiglu_q4k_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "ffn_swiglu_q4k": (_I, [_VP, _VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP, _I, _I, _VP,
                             _VP, _SZ, _VP]),
+    "ffn_swiglu_q4k_noalloc": (_I, [_VP, _VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP, _I, _I, _VP,
+                                    _VP]),
 }
+
+#: Bytes of the fixed per-device scratch buffer of ffn_swiglu_q4k_noalloc.
+Q4K_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 
 def load_library(path: str | None = None) -> ctypes.CDLL:
@@ -225,3 +230,20 @@ def ffn_swiglu_q4k(w_gate, w_up, w_down, x, x_dtype: int, m: int, hidden: int, i
         (y, 4 * m * hidden if ok else 0, _F32, "y"), (workspace, 0, None, "workspace"))
     _check(load_library().ffn_swiglu_q4k(pg, pu, pd, n_experts, px, x_dtype, m, hidden, inter, pi, pt,
                                          top_k, regime, py, pws, ws_bytes, _stream(stream)))
+
+
+def ffn_swiglu_q4k_noalloc(w_gate, w_up, w_down, x, x_dtype: int, m: int, hidden: int, inter: int,
+                           y, n_experts: int = 1, ids=None, wts=None, top_k: int = 0,
+                           regime: int = Q4K_REGIME_AUTO, stream=None) -> None:
+    """ffn_swiglu_q4k on the library's fixed scratch buffer (no workspace)."""
+    ok = _pos(m, hidden, inter, n_experts)
+    gu = n_experts * q4k_weight_bytes(inter, hidden) if ok else 0
+    dn = n_experts * q4k_weight_bytes(hidden, inter) if ok else 0
+    pairs = m * top_k if ok and ids is not None and top_k > 0 else 0
+    pg, pu, pd, px, pi, pt, py = _ptrs(
+        (w_gate, gu, _BYTES, "w_gate"), (w_up, gu, _BYTES, "w_up"), (w_down, dn, _BYTES, "w_down"),
+        (x, _x_size(x_dtype) * m * hidden if ok else 0, _x_dtypes(x_dtype), "x"),
+        (ids, 4 * pairs, _I32, "ids"), (wts, 4 * pairs, _F32, "wts"),
+        (y, 4 * m * hidden if ok else 0, _F32, "y"))
+    _check(load_library().ffn_swiglu_q4k_noalloc(pg, pu, pd, n_experts, px, x_dtype, m, hidden, inter,
+                                                 pi, pt, top_k, regime, py, _stream(stream)))

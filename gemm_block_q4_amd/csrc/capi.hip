@@ -189,6 +189,7 @@ const char* q4k_status_string(int status) {
     case Q4K_ERR_WORKSPACE: return "workspace missing or too small";
     case Q4K_ERR_LAUNCH: return "the HIP runtime reported a launch error";
     case Q4K_ERR_DEVICE: return "the current device is not gfx950";
+    case Q4K_ERR_SCRATCH: return "the call needs more scratch than the allocation-free entry point's fixed buffer holds";
     default: return "unknown status";
   }
 }
@@ -331,10 +332,37 @@ size_t ffn_swiglu_q4k_workspace_bytes(int m, int hidden, int inter, int top_k, i
   return L.total;
 }
 
-int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int n_experts,
-                   const void* x, int x_dtype, int m, int hidden, int inter, const int32_t* ids,
-                   const float* wts, int top_k, int regime, float* y, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Scratch memory of the allocation-free FFN entry point: one copy per device
+// (the loader places it in each device's memory with the code object).  Host
+// code never passes `scratch` itself to a kernel (on the host it names a
+// stand-in, not the device copy); it resolves the device address once per
+// device with hipGetSymbolAddress and passes that.
+static __device__ __align__(256) uint8_t scratch[Q4K_NOALLOC_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device (nullptr on error).
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+// ffn_swiglu_q4k with the caller's workspace, or (use_scratch) with the
+// library's fixed scratch buffer of the current device.
+int ffn_common(const void* w_gate, const void* w_up, const void* w_down, int n_experts,
+               const void* x, int x_dtype, int m, int hidden, int inter, const int32_t* ids,
+               const float* wts, int top_k, int regime, float* y, void* workspace,
+               size_t workspace_bytes, bool use_scratch, void* stream) {
   if (!w_gate || !w_up || !w_down || !x || !y) return Q4K_ERR_NULL;
   if (x_dtype != Q4K_F32 && x_dtype != Q4K_BF16) return Q4K_ERR_SHAPE;
   if (m < 1 || n_experts < 1) return Q4K_ERR_SHAPE;
@@ -366,12 +394,21 @@ int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int
   if (moe && ((st = check_elems(m * top_k, hidden)) || (st = check_elems(m * top_k, inter)))) return st;
   FfnLayout L;
   if (!ffn_layout(m, hidden, inter, top_k, reg, &L)) return Q4K_ERR_SHAPE;
-  if (!workspace || workspace_bytes < L.total) return Q4K_ERR_WORKSPACE;
+  if (use_scratch) {
+    if (L.total > Q4K_NOALLOC_SCRATCH_BYTES) return Q4K_ERR_SCRATCH;
+  } else if (!workspace || workspace_bytes < L.total) {
+    return Q4K_ERR_WORKSPACE;
+  }
   if (!aligned(w_gate, kAlign) || !aligned(w_up, kAlign) || !aligned(w_down, kAlign) ||
-      !aligned(x, kAlign) || !aligned(y, 4) || !aligned(workspace, kAlign) ||
+      !aligned(x, kAlign) || !aligned(y, 4) || (!use_scratch && !aligned(workspace, kAlign)) ||
       (ids && !aligned(ids, 4)) || (wts && !aligned(wts, 4)))
     return Q4K_ERR_ALIGN;
   if ((st = check_device())) return st;
+  if (use_scratch) {
+    workspace = scratch_ptr();
+    if (!workspace) return Q4K_ERR_LAUNCH;
+    workspace_bytes = Q4K_NOALLOC_SCRATCH_BYTES;
+  }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -508,6 +545,26 @@ int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int
   dn.split_stride = plane;
   if ((e = launch_mmq(dn, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
   return launch_status(launch_mmq_split_reduce(parts, splits, plane, plane, y, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int n_experts,
+                   const void* x, int x_dtype, int m, int hidden, int inter, const int32_t* ids,
+                   const float* wts, int top_k, int regime, float* y, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return ffn_common(w_gate, w_up, w_down, n_experts, x, x_dtype, m, hidden, inter, ids, wts, top_k,
+                    regime, y, workspace, workspace_bytes, false, stream);
+}
+
+int ffn_swiglu_q4k_noalloc(const void* w_gate, const void* w_up, const void* w_down, int n_experts,
+                           const void* x, int x_dtype, int m, int hidden, int inter,
+                           const int32_t* ids, const float* wts, int top_k, int regime, float* y,
+                           void* stream) {
+  return ffn_common(w_gate, w_up, w_down, n_experts, x, x_dtype, m, hidden, inter, ids, wts, top_k,
+                    regime, y, nullptr, 0, true, stream);
 }
 
 }  // extern "C"

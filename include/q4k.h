@@ -68,6 +68,9 @@ extern "C" {
 #define Q4K_Q8_1_BLOCK 32
 /* Most tokens the decode regime (dequant-fused GEMV) takes per call. */
 #define Q4K_DECODE_MAX_TOKENS 8
+/* Bytes of the fixed scratch buffer behind ffn_swiglu_q4k_noalloc (64 MiB
+   per device). */
+#define Q4K_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
 
 typedef enum {
   Q4K_OK = 0,
@@ -77,7 +80,8 @@ typedef enum {
   Q4K_ERR_OVERFLOW = 4,  /* a derived size overflows */
   Q4K_ERR_WORKSPACE = 5, /* workspace NULL or smaller than required */
   Q4K_ERR_LAUNCH = 6,    /* the HIP runtime reported an error for a launch */
-  Q4K_ERR_DEVICE = 7     /* the current device is not gfx950 */
+  Q4K_ERR_DEVICE = 7,    /* the current device is not gfx950 */
+  Q4K_ERR_SCRATCH = 8    /* needs more than Q4K_NOALLOC_SCRATCH_BYTES (ffn_swiglu_q4k_noalloc) */
 } q4k_status;
 
 typedef enum { Q4K_F32 = 0, Q4K_BF16 = 1 } q4k_dtype;
@@ -240,6 +244,25 @@ int ffn_swiglu_q4k(const void* w_gate, const void* w_up, const void* w_down, int
                    const void* x, int x_dtype, int m, int hidden, int inter,
                    const int32_t* ids, const float* wts, int top_k, int regime, float* y,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Allocation-free form of ffn_swiglu_q4k, for callers that cannot allocate
+   device memory or pass a workspace (code under HIP graph capture, tight
+   serving loops, harnesses that forbid hipMalloc).  Same arguments, results
+   and errors as ffn_swiglu_q4k, without workspace / workspace_bytes: the
+   intermediate buffers live in a fixed scratch array of
+   Q4K_NOALLOC_SCRATCH_BYTES in device memory, one per device, held until the
+   process ends.  A call whose layout (ffn_swiglu_q4k_workspace_bytes for the
+   same sizes and regime) exceeds it returns Q4K_ERR_SCRATCH and launches
+   nothing; e.g. 512 tokens of the 5120/17408 prefill need 48.6 MB.  The call
+   itself allocates nothing and calls no allocating routine.  Every call on a
+   device shares that device's scratch (no result depends on what a previous
+   call left there), so calls that overlap on one device -- on different
+   streams, or from different host threads without ordering -- race and must
+   not be issued. */
+int ffn_swiglu_q4k_noalloc(const void* w_gate, const void* w_up, const void* w_down,
+                           int n_experts, const void* x, int x_dtype, int m, int hidden,
+                           int inter, const int32_t* ids, const float* wts, int top_k, int regime,
+                           float* y, void* stream);
 
 #ifdef __cplusplus
 }

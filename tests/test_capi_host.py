@@ -35,7 +35,7 @@ def test_exports_every_declared_function(lib):
     assert {"q4k_gemv", "q8_1_quantize", "q4k_mmq", "ffn_swiglu_q4k", "q4k_weight_bytes",
             "q4k_status_string", "ffn_swiglu_q4k_workspace_bytes",
             "q4k_test_mmq_partials", "q4k_q8_gemv", "q4k_quantize", "q6k_gemv",
-            "q6k_weight_bytes", "q4k_mmq_bf16"} <= set(names)
+            "q6k_weight_bytes", "q4k_mmq_bf16", "ffn_swiglu_q4k_noalloc"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -48,7 +48,7 @@ def test_weight_bytes_matches_oracle(lib):
 
 
 def test_status_strings(lib):
-    for s in range(0, 8):
+    for s in range(0, 9):
         assert lib.q4k_status_string(s)
     assert lib.q4k_status_string(99) == b"unknown status"
 
@@ -175,3 +175,17 @@ def test_mmq_bf16_validation(lib):
     assert f(P, P, P, P + 1, 4, 64, 256, None) == 3     # bf16 output needs 2 bytes
     assert f(P, P, P, P, 4, 64, 300, None) == 2         # k not a multiple of 256
     assert f(P, P, P, P, 0, 64, 256, None) == 2
+
+
+def test_ffn_noalloc_validation(lib):
+    f = lib.ffn_swiglu_q4k_noalloc
+    # the same argument checks as ffn_swiglu_q4k, without a workspace
+    assert f(None, P, P, 1, P, 0, 1, 256, 768, None, None, 0, 0, P, None) == 1
+    assert f(P, P, P, 1, P, 0, 1, 300, 768, None, None, 0, 0, P, None) == 2
+    assert f(P + 4, P, P, 1, P, 0, 1, 256, 768, None, None, 0, 0, P, None) == 3
+    # a layout beyond the fixed scratch (4096 tokens of 5120/17408 need about
+    # 390 MB) is refused before any HIP call
+    assert lib.ffn_swiglu_q4k_workspace_bytes(4096, 5120, 17408, 0, 0) > B.Q4K_NOALLOC_SCRATCH_BYTES
+    assert f(P, P, P, 1, P, 1, 4096, 5120, 17408, None, None, 0, 0, P, None) == 8
+    # 512 tokens of the same FFN fit
+    assert lib.ffn_swiglu_q4k_workspace_bytes(512, 5120, 17408, 0, 0) <= B.Q4K_NOALLOC_SCRATCH_BYTES
