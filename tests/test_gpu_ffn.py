@@ -90,6 +90,18 @@ def test_decode_regime_forced_m8_matches(lib):
     assert orc.relative_l2(y, orc.ffn_decode(wg, wu, wd, hidden, inter, x)) <= TOL
 
 
+@pytest.mark.parametrize("m", [1, 3])
+def test_decode_ffn_wide_inter(lib, m):
+    # inter 18432 > 16384: the down pass's one-token rows span five wavefronts
+    # with four activation units per thread and LDS above 64 KiB
+    hidden, inter = 512, 18432
+    say(f"ffn decode wide inter {hidden}/{inter} m={m}")
+    wg, wu, wd = synth.dense_ffn_weights(95, hidden, inter)
+    x = synth.activations(95, m, hidden, outliers=True, sub=m)
+    y = ffn_gpu(lib, wg, wu, wd, x, hidden, inter)
+    assert orc.relative_l2(y, orc.ffn_decode(wg, wu, wd, hidden, inter, x)) <= TOL
+
+
 @pytest.mark.parametrize("m", [1, 4, 8])
 def test_decode_q8_ffn_7b(lib, decode7b, m):
     # Q8_1 decode regime: the prefill arithmetic (Q8_1 of x and of h) on the
@@ -176,6 +188,20 @@ def test_moe_duplicates_and_out_of_range_ids(lib):
     valid = (ids >= 0) & (ids < n_exp)
     ref = orc.moe_decode(*banks, n_exp, hidden, inter, x, np.where(valid, ids, 0),
                          np.where(valid, wts, 0).astype(np.float32))
+    assert orc.relative_l2(y, ref) <= TOL
+
+
+@pytest.mark.parametrize("inter", [3072, 4096])
+def test_moe_top8_wide_down(lib, inter):
+    # top-8 with down rows of 48 or 64 slices: the fused down pass holds eight
+    # wavefronts' digits and the slot results in more than 64 KiB of LDS
+    n_exp, hidden, m, k = 10, 512, 3, 8
+    say(f"moe top-8 {hidden}/{inter}")
+    banks = synth.moe_banks(96, n_exp, hidden, inter)
+    x = synth.activations(96, m, hidden, outliers=True)
+    ids, wts = synth.router(96, m, n_exp, k)
+    y = moe_gpu(lib, banks, x, ids, wts, n_exp, hidden, inter)
+    ref = orc.moe_decode(*banks, n_exp, hidden, inter, x, ids, wts)
     assert orc.relative_l2(y, ref) <= TOL
 
 

@@ -46,6 +46,16 @@ def test_gemv_multi_token_tiles(lib, m, n, k):
     check(lib, w, x, n, k)
 
 
+@pytest.mark.parametrize("n,k", [(301, 16384), (77, 20480), (45, 32768)])
+def test_gemv_one_token_wide_k(lib, n, k):
+    # one token, rows of 64..128 slices: two or four activation units per
+    # thread, and the digits of x take more than 64 KiB of LDS from k = 20480
+    say(f"gemv one token wide k n={n} k={k}")
+    w = synth.random_q4k(synth.rng(73, 1, n + k), n, k)
+    x = synth.activations(73, 1, k, outliers=True, sub=n)
+    check(lib, w, x, n, k)
+
+
 @pytest.mark.parametrize("shape", [0, 1, 2])
 def test_gemv_sweep_full_size(lib, shape):
     n, k, w, x = synth.gemv_sweep_case(shape)
