@@ -13,8 +13,11 @@ Also reported (``secondary``): the 7B-style decode FFN at 1/4/8 tokens, the
 prefill FFN (Q8_1 + MMQ) at 512 and 2048 tokens in TOPS, the 64-expert top-8
 MoE decode FFN, the Q8_1-activation GEMV (q4k_q8_gemv) on the sweep shapes at
 1/4/8 tokens, the load-time Q4_K quantiser, and the roofline of the dominant
-kernel.  ``cpu_baseline``
-times the CPU oracle on a bounded sample of the headline workload.
+kernel with the plain-read ceiling of the same bytes (q4k_test_read) beside
+it.  Every per-call figure is the median of 5 replays of a graph of calls.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the headline
+workload, on all BLAS threads and on one, with the host's CPU model and core
+count.
 """
 
 from __future__ import annotations
@@ -45,6 +48,12 @@ TRAFFIC_SOURCES = {
     "gemm_block_q4_amd/csrc/q4k_device.hpp":
         "532c6e881bd56ddab7a0e075b479fbab8468380451639a48865dc41a8cb9352e",
 }
+
+
+# the kernel the roofline describes (one token, dense): layout 1 (a row is one
+# wavefront) for k = 4096, layout 2 (a row spans wavefronts) for k = 11008
+GEMV_KERNEL = ("gemv_d4_kernel<false, false, 0, 1|2, 1|2, 4> (q4k_gemv, m=1; layout 1 for k=4096, "
+               "2 for k=11008)")
 
 
 def log(*a):
@@ -130,6 +139,23 @@ def timed_graph(fn, steps, warmup):
     return t.ms
 
 
+TRIALS = 5
+
+
+def median_us(fn, reps, trials=TRIALS):
+    """Median over `trials` replays of one graph of `reps` calls fn(i) (after
+    one untimed replay): microseconds per call, with the trials' spread."""
+    g = capture(fn, reps)
+    g.replay()
+    per = []
+    for _ in range(trials):
+        with Timer() as t:
+            g.replay()
+        per.append(t.ms * 1e3 / reps)
+    per.sort()
+    return per[len(per) // 2], per[0], per[-1]
+
+
 # -- headline: GEMV sweep -----------------------------------------------------------
 
 def gemv_sweep(q4k, synth, steps, warmup):
@@ -148,7 +174,10 @@ def gemv_sweep(q4k, synth, steps, warmup):
 
     ms = timed_graph(one_pass, steps, warmup)
     total_bytes = steps * sum(sh["bytes"] for sh in shapes)
-    # per-shape average launch duration (graph of launches of one shape)
+    # per-shape launch duration (median of 5 replays of a graph of launches
+    # of one shape over the rotated copies), and the plain-read ceiling: the
+    # same bytes of the same copies streamed by q4k_test_read
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     per_shape = []
     for sh in shapes:
         reps = len(sh["w"])
@@ -156,13 +185,14 @@ def gemv_sweep(q4k, synth, steps, warmup):
         def one(i, sh=sh):
             q4k.q4k_gemv(sh["w"][i % len(sh["w"])], sh["x"], sh["y"], 1, sh["n"], sh["k"])
 
-        g = capture(one, reps)
-        g.replay()
-        with Timer() as t:
-            g.replay()
-        us = t.ms * 1e3 / reps
-        per_shape.append(dict(n=sh["n"], k=sh["k"], bytes=sh["bytes"], us=us,
-                              gbs=sh["bytes"] / (us * 1e-6) / 1e9))
+        def read(i, sh=sh):
+            q4k.q4k_test_read(sh["w"][i % len(sh["w"])], sh["bytes"], sink)
+
+        us, us_lo, us_hi = median_us(one, reps)
+        rd, _, _ = median_us(read, reps)
+        per_shape.append(dict(n=sh["n"], k=sh["k"], bytes=sh["bytes"], us=us, us_min=us_lo, us_max=us_hi,
+                              gbs=sh["bytes"] / (us * 1e-6) / 1e9, read_us=rd,
+                              read_gbs=sh["bytes"] / (rd * 1e-6) / 1e9))
     return ms, total_bytes, per_shape
 
 
@@ -191,8 +221,7 @@ def decode_ffn(q4k, synth, reps=40):
                 q4k.ffn_swiglu_q4k(c[:gb], c[gb:2 * gb], c[2 * gb:], x, q4k.Q4K_F32, m, hidden, inter,
                                    y, ws, regime=regime)
 
-            ms = timed_graph(call, reps, 5)
-            us = ms * 1e3 / reps
+            us, _, _ = median_us(call, reps)
             out[f"{tag}m{m}"] = dict(us_per_ffn=round(us, 2), tokens_per_s=round(m / (us * 1e-6), 1),
                                      weight_gbs=round(per_ffn / (us * 1e-6) / 1e9, 1))
     return out
@@ -219,9 +248,7 @@ def q8_gemv(q4k, synth):
             def call(i, copies=copies, qs=qs, ds=ds, y=y, m=m, n=n, k=k):
                 q4k.q4k_q8_gemv(copies[i % len(copies)], qs, ds, y, m, n, k)
 
-            reps = len(copies)
-            ms = timed_graph(call, reps, reps)
-            us = ms * 1e3 / reps
+            us, _, _ = median_us(call, len(copies))
             out[f"n{n}_k{k}_m{m}"] = dict(us=round(us, 2), weight_gbs=round(nbytes / (us * 1e-6) / 1e9, 1))
     return out
 
@@ -243,9 +270,7 @@ def quantize_q4k(q4k, synth):
         def call(i, src=src, dt=dt):
             q4k.q4k_quantize(src[i % len(src)], dt, rows, cols, w)
 
-        reps = len(src)
-        ms = timed_graph(call, reps, reps)
-        us = ms * 1e3 / reps
+        us, _, _ = median_us(call, len(src))
         moved = arr.nbytes + out_bytes
         res[name] = dict(us=round(us, 2), gbs=round(moved / (us * 1e-6) / 1e9, 1))
     return res
@@ -266,9 +291,7 @@ def lm_head_q6k(q4k, synth):
     def call(i):
         q4k.q6k_gemv(copies[i % len(copies)], xd, y, n, k)
 
-    reps = 4 * len(copies)
-    ms = timed_graph(call, reps, len(copies))
-    us = ms * 1e3 / reps
+    us, _, _ = median_us(call, 4 * len(copies))
     return dict(us=round(us, 2), weight_gbs=round(nbytes / (us * 1e-6) / 1e9, 1),
                 frac_hbm_peak=round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4))
 
@@ -293,8 +316,7 @@ def mmq_store(q4k, synth, reps=4):
         def call(i, fn=fn, y=y):
             fn(copies[i % len(copies)], qs, ds, y, m, n, k)
 
-        ms = timed_graph(call, reps, 1)
-        us = ms * 1e3 / reps
+        us, _, _ = median_us(call, reps)
         out[name] = dict(us=round(us, 1), tops=round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1))
     return out
 
@@ -318,8 +340,7 @@ def prefill_ffn(q4k, synth, reps=4):
             q4k.ffn_swiglu_q4k(c[:gb], c[gb:2 * gb], c[2 * gb:], x, q4k.Q4K_BF16, m, hidden, inter,
                                y, ws)
 
-        ms = timed_graph(call, reps, 1)
-        us = ms * 1e3 / reps
+        us, _, _ = median_us(call, reps)
         ops = 2.0 * m * (3 * hidden * inter)
         out[f"m{m}"] = dict(us_per_ffn=round(us, 1), tops=round(ops / (us * 1e-6) / 1e12, 1),
                             frac_int8_peak=round(ops / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4),
@@ -348,8 +369,7 @@ def moe_ffn(q4k, synth, reps=40):
         q4k.ffn_swiglu_q4k(c[:bank], c[bank:2 * bank], c[2 * bank:], x, q4k.Q4K_F32, m, hidden,
                            inter, y, ws, n_experts=n_exp, ids=ids, wts=wts, top_k=k)
 
-    ms = timed_graph(call, reps, 5)
-    us = ms * 1e3 / reps
+    us, _, _ = median_us(call, reps)
     return dict(distinct_experts=distinct, us_per_ffn=round(us, 2),
                 tokens_per_s=round(m / (us * 1e-6), 1),
                 weight_gbs=round(distinct * per_expert / (us * 1e-6) / 1e9, 1))
@@ -357,28 +377,61 @@ def moe_ffn(q4k, synth, reps=40):
 
 # -- CPU oracle baseline ---------------------------------------------------------------
 
-def cpu_baseline(synth):
-    from oracle import q4k_oracle as orc
+def cpu_info():
+    """Host CPU model (from /proc/cpuinfo, as lscpu reports it) and the cores this
+    process may run on (what nproc prints)."""
+    model = "unknown"
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
-    cases = [synth.gemv_sweep_case(s) for s in range(3)]
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count() or 1
+    return model, nproc
+
+
+def cpu_oracle_rate(orc, cases, seconds):
+    """Weight-GB/s of the oracle GEMV over passes of the sweep for about `seconds`."""
     total = 0
-    t0 = time.perf_counter()
     passes = 0
+    t0 = time.perf_counter()
     while True:
         for n, k, w, x in cases:
             orc.gemv(w, n, k, x)
             total += orc.q4k_weight_bytes(n, k)
         passes += 1
-        if time.perf_counter() - t0 > 12.0:
+        if time.perf_counter() - t0 > seconds:
             break
     dt = time.perf_counter() - t0
-    return dict(value=round(total / dt / 1e9, 3), unit="GB/s", cores=cores, kind="oracle",
-                sample=f"{passes} pass(es) of the 3-shape batch-1 GEMV sweep through the f64 "
-                       f"numpy oracle (dequantise + matmul), {dt:.1f} s")
+    return total / dt / 1e9, passes, dt
+
+
+def cpu_baseline(synth):
+    """The f64 numpy oracle (dequantise, then a BLAS matrix-vector product) on
+    the batch-1 GEMV sweep, once with every BLAS thread of the host and once
+    on one thread.  The oracle is a correctness reference, untuned."""
+    from oracle import q4k_oracle as orc
+    from threadpoolctl import threadpool_info, threadpool_limits
+    model, nproc = cpu_info()
+    blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    cases = [synth.gemv_sweep_case(s) for s in range(3)]
+    all_rate, all_passes, all_dt = cpu_oracle_rate(orc, cases, 8.0)
+    with threadpool_limits(limits=1):
+        one_rate, one_passes, one_dt = cpu_oracle_rate(orc, cases, 8.0)
+    return dict(value=round(all_rate, 3), unit="GB/s", cores=blas_threads, kind="oracle",
+                sample=f"{all_passes} pass(es) of the 3-shape batch-1 GEMV sweep through the f64 "
+                       f"numpy oracle (dequantise + matmul) on {blas_threads} BLAS threads, "
+                       f"{all_dt:.1f} s; the dequantisation itself runs on one thread",
+                single_thread=dict(value=round(one_rate, 3), unit="GB/s", cores=1,
+                                   sample=f"{one_passes} pass(es), {one_dt:.1f} s"),
+                nproc=nproc, cpu_model=model,
+                note="plain f64 correctness oracle, not a tuned CPU kernel")
 
 
 def main():
@@ -411,12 +464,27 @@ def main():
 
     sum_bytes = sum(p["bytes"] for p in per_shape)
     sum_us = sum(p["us"] for p in per_shape)
+    sum_read = sum(p["read_us"] for p in per_shape)
     achieved = sum_bytes / (sum_us * 1e-6) / 1e9
+    read_gbs = sum_bytes / (sum_read * 1e-6) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(),
                     traffic_scope="HBM bytes of the three sweep launches (same scope as achieved)",
-                    kernel="gemv_d4_kernel<false, false, 0, 1|2, 1|2, 4> (q4k_gemv, m=1; layout 1 for k=4096, 2 for k=11008)",
-                    per_shape=[dict(n=p["n"], k=p["k"], us=round(p["us"], 3), gbs=round(p["gbs"], 1))
+                    kernel=GEMV_KERNEL,
+                    timing=f"per shape: median of {TRIALS} replays of a graph of launches over the "
+                           "rotated copies (HIP events on the launch stream)",
+                    read_ceiling_gbs=round(read_gbs, 1),
+                    frac_of_read_ceiling=round(achieved / read_gbs, 4),
+                    read_ceiling_note="q4k_test_read: one 16-byte load per thread over the same "
+                                      "bytes of the same copies, timed the same way; a 70% of 8 TB/s "
+                                      "target below the read ceiling's time is out of reach of any "
+                                      "single launch",
+                    per_shape=[dict(n=p["n"], k=p["k"], us=round(p["us"], 3),
+                                    us_min=round(p["us_min"], 3), us_max=round(p["us_max"], 3),
+                                    gbs=round(p["gbs"], 1), read_us=round(p["read_us"], 3),
+                                    read_gbs=round(p["read_gbs"], 1),
+                                    frac_of_read_ceiling=round(p["read_us"] / p["us"], 4),
+                                    target_us_70pct_hbm=round(p["bytes"] / (0.7 * HBM_PEAK_GBS * 1e3), 3))
                                for p in per_shape])
 
     secondary = {}

@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     q4k_q8_gemv,
     q4k_quantize,
     q4k_test_mmq_partials,
+    q4k_test_read,
     q4k_weight_bytes,
     q6k_gemv,
     q6k_weight_bytes,

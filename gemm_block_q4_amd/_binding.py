@@ -48,6 +48,7 @@ _SIGNATURES = {
     "ffn_swiglu_q4k_workspace_bytes": (_SZ, [_I, _I, _I, _I, _I]),
     "ffn_swiglu_q4k": (_I, [_VP, _VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP, _I, _I, _VP,
                             _VP, _SZ, _VP]),
+    "q4k_test_read": (_I, [_VP, _SZ, _VP, _VP]),
     "ffn_swiglu_q4k_noalloc": (_I, [_VP, _VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP, _I, _I, _VP,
                                     _VP]),
 }
@@ -247,3 +248,9 @@ def ffn_swiglu_q4k_noalloc(w_gate, w_up, w_down, x, x_dtype: int, m: int, hidden
         (y, 4 * m * hidden if ok else 0, _F32, "y"))
     _check(load_library().ffn_swiglu_q4k_noalloc(pg, pu, pd, n_experts, px, x_dtype, m, hidden, inter,
                                                  pi, pt, top_k, regime, py, _stream(stream)))
+
+
+def q4k_test_read(buf, nbytes: int, sink, stream=None) -> None:
+    """Plain read of the first ``nbytes`` bytes of ``buf`` (read-ceiling hook)."""
+    pb, ps = _ptrs((buf, nbytes, None, "buf"), (sink, 4, _I32, "sink"))
+    _check(load_library().q4k_test_read(pb, nbytes, ps, _stream(stream)))

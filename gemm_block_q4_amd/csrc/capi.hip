@@ -326,6 +326,16 @@ int q4k_test_mmq_partials(const void* w, const int8_t* qs, int m, int n, int k,
   return mmq_common(w, qs, nullptr, nullptr, nullptr, partials, m, n, k, stream);
 }
 
+int q4k_test_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return Q4K_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0) return Q4K_ERR_SHAPE;
+  if (bytes / 16 / 256 >= 0x7FFFFFFFu) return Q4K_ERR_OVERFLOW;
+  if (!aligned(buf, kAlign) || !aligned(sink, 4)) return Q4K_ERR_ALIGN;
+  const int st = check_device();
+  if (st) return st;
+  return launch_status(launch_read_ceiling(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 size_t ffn_swiglu_q4k_workspace_bytes(int m, int hidden, int inter, int top_k, int regime) {
   FfnLayout L;
   if (!ffn_layout(m, hidden, inter, top_k, regime, &L)) return 0;

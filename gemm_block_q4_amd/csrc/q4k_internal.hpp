@@ -104,6 +104,10 @@ int mmq_choose_splits(int m, int n, int k, int max_splits, int cus);
 hipError_t launch_mmq_split_reduce(const float* parts, int splits, size_t stride, size_t count,
                                    float* y, hipStream_t stream);
 
+// Plain read of `bytes` (a multiple of 16, 16-byte aligned) from `buf`, one
+// 16-byte load per thread; `sink` is written only for a fixed bit pattern.
+hipError_t launch_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 // y[t] = sum_{s < top_k} wts[t][s] * y_pair[t * top_k + s] in slot order
 // (pairs with an id outside [0, n_experts) skipped).
 hipError_t launch_moe_combine(const float* y_pair, const float* wts, const int32_t* ids, int m,

@@ -210,6 +210,16 @@ int q6k_gemv(const void* w, const float* x, float* y, int n, int k, void* stream
 int q4k_test_mmq_partials(const void* w, const int8_t* qs, int m, int n, int k,
                           int32_t* partials, void* stream);
 
+/* Measurement hook: reads `bytes` bytes of device memory at `buf` the
+   plainest way (one 16-byte load per thread, 256 threads per workgroup) and
+   discards them; `sink` (device, one uint32) is written only if a lane's 16
+   bytes XOR to 0x9E3779B9.  Timed beside q4k_gemv on the same weight copies
+   it gives the read ceiling the GEMV is compared with; not part of the
+   computation.  bytes > 0 and a multiple of 16; buf 16-byte aligned.
+   Errors: Q4K_ERR_NULL, Q4K_ERR_SHAPE, Q4K_ERR_ALIGN, Q4K_ERR_OVERFLOW,
+   Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */
+int q4k_test_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Host.  Workspace bytes ffn_swiglu_q4k needs for these sizes and regime
    (Q4K_REGIME_AUTO resolves by m as the call does); top_k = 0 for a dense
    FFN.  Returns 0 for invalid sizes. */

@@ -35,7 +35,8 @@ def test_exports_every_declared_function(lib):
     assert {"q4k_gemv", "q8_1_quantize", "q4k_mmq", "ffn_swiglu_q4k", "q4k_weight_bytes",
             "q4k_status_string", "ffn_swiglu_q4k_workspace_bytes",
             "q4k_test_mmq_partials", "q4k_q8_gemv", "q4k_quantize", "q6k_gemv",
-            "q6k_weight_bytes", "q4k_mmq_bf16", "ffn_swiglu_q4k_noalloc"} <= set(names)
+            "q6k_weight_bytes", "q4k_mmq_bf16", "ffn_swiglu_q4k_noalloc",
+            "q4k_test_read"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -189,3 +190,13 @@ def test_ffn_noalloc_validation(lib):
     assert f(P, P, P, 1, P, 1, 4096, 5120, 17408, None, None, 0, 0, P, None) == 8
     # 512 tokens of the same FFN fit
     assert lib.ffn_swiglu_q4k_workspace_bytes(512, 5120, 17408, 0, 0) <= B.Q4K_NOALLOC_SCRATCH_BYTES
+
+
+def test_read_hook_validation(lib):
+    r = lib.q4k_test_read
+    assert r(None, 16, P, None) == 1
+    assert r(P, 16, None, None) == 1
+    assert r(P, 0, P, None) == 2
+    assert r(P, 24, P, None) == 2        # not a multiple of 16
+    assert r(P + 8, 16, P, None) == 3
+    assert r(P, 16, P + 2, None) == 3
