@@ -43,6 +43,7 @@
 // them with the routing weights (down projection plus the combine).
 #include <algorithm>
 
+#include "lane_reduce.hpp"
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
 
@@ -69,66 +70,32 @@ __device__ __forceinline__ float4 load_x4(rsrc_t r, uint32_t off) {
   }
 }
 
-// The quarter of one block a lane streams per row.  The four lanes of a
-// block are an aligned lane quad; lane g of the quad loads header word g and
-// the quad shares the four words by DPP broadcasts (one 4-byte load per lane
-// instead of the 16-byte header four times).
+// What a lane streams per row: the 16-byte header of its block (the four
+// lanes of a block load the same 16 bytes, one cache line) and quant bytes
+// 32g .. 32g+31 of its quarter g.
 struct RawSlice {
-  uint32_t hw;   // header word g of the block
+  uint4 h;       // d | dmin << 16, scales[0..3], scales[4..7], scales[8..11]
   uint4 q0, q1;  // quant bytes 32g .. 32g+31
 };
 
-struct Slice {
-  uint32_t h;   // d | dmin << 16
-  uint32_t s0;  // scales[0..3]
-  uint32_t s1;  // scales[4..7]
-  uint32_t s2;  // scales[8..11]
-  uint4 q0, q1; // quant bytes 32g .. 32g+31
-};
-
-// Slice g of the block at byte offset `off` of the resource (kOob: zeros).
-__device__ __forceinline__ void load_slice(rsrc_t r, uint32_t off, int g, RawSlice& s) {
-  const uint32_t q = off + 32u * static_cast<uint32_t>(g);
-  s.hw = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off + 4u * g), 0, 0));
-  s.q0 = buf_load16(r, q + 16u);
-  s.q1 = buf_load16(r, q + 32u);
-}
-
-// Lane permutes on the VALU (no LDS round trip).  Lanes whose source is out of
-// range read 0.
-template <int CTRL, int ROW_MASK = 0xF>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                               ROW_MASK, 0xF, true));
-}
-
-// Word i of the lane's quad, in every lane of the quad (quad_perm(i,i,i,i)).
-template <int I>
-__device__ __forceinline__ uint32_t quad_bcast(uint32_t v) {
-  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), I * 0x55, 0xF, 0xF, true));
-}
-
-__device__ __forceinline__ Slice expand(const RawSlice& r) {
-  Slice s;
-  s.h = quad_bcast<0>(r.hw);
-  s.s0 = quad_bcast<1>(r.hw);
-  s.s1 = quad_bcast<2>(r.hw);
-  s.s2 = quad_bcast<3>(r.hw);
-  s.q0 = r.q0;
-  s.q1 = r.q1;
-  return s;
+// Block at byte offset `off` of the resource; qoff = 16 + 32g.  An offset at
+// or past the resource's size reads zeros (no memory request).
+__device__ __forceinline__ void load_slice(rsrc_t r, uint32_t off, uint32_t qoff, RawSlice& s) {
+  s.h = buf_load16(r, off);
+  s.q0 = buf_load16(r, off + qoff);
+  s.q1 = buf_load16(r, off + qoff + 16u);
 }
 
 // Sum over aligned segments of SEG lanes (SEG a power of two <= 64); the
 // total lands in the last lane of each segment.
 template <int SEG>
 __device__ __forceinline__ float segment_sum(float v) {
-  if constexpr (SEG >= 2) v += dpp<0xB1>(v);        // quad_perm(1,0,3,2)
-  if constexpr (SEG >= 4) v += dpp<0x4E>(v);        // quad_perm(2,3,0,1)
-  if constexpr (SEG >= 8) v += dpp<0x114>(v);       // row_shr:4
-  if constexpr (SEG >= 16) v += dpp<0x118>(v);      // row_shr:8
-  if constexpr (SEG >= 32) v += dpp<0x142, 0xA>(v); // row_bcast:15 into rows 1, 3
-  if constexpr (SEG >= 64) v += dpp<0x143, 0xC>(v); // row_bcast:31 into rows 2, 3
+  if constexpr (SEG >= 2) v += dpp_f<0xB1>(v);        // quad_perm(1,0,3,2)
+  if constexpr (SEG >= 4) v += dpp_f<0x4E>(v);        // quad_perm(2,3,0,1)
+  if constexpr (SEG >= 8) v += dpp_f<0x114>(v);       // row_shr:4
+  if constexpr (SEG >= 16) v += dpp_f<0x118>(v);      // row_shr:8
+  if constexpr (SEG >= 32) v += dpp_f<0x142, 0xA>(v); // row_bcast:15 into rows 1, 3
+  if constexpr (SEG >= 64) v += dpp_f<0x143, 0xC>(v); // row_bcast:31 into rows 2, 3
   return v;
 }
 
@@ -144,37 +111,38 @@ __device__ __forceinline__ float segment_sum_rt(float v, int seg) {
   }
 }
 
-// Per-lane constants of the 6-bit field extraction for sub-blocks 2g, 2g+1:
-// byte u = (2g) & 3 of the scale words, and whether the pair is in the upper
-// half (sub-blocks 4..7).
+// Per-lane byte selectors that gather the 6-bit (scale, min) fields of
+// sub-blocks 2g and 2g+1 from the header without a branch.  With u = 2g mod 4
+// (the byte of sub-block 2g within a scale word):
+//   P = [scales[u], scales[u+1], scales[u+4], scales[u+5]]  (v_perm of words 1, 2)
+//   lower quarters (g < 2): the fields are the low 6 bits of P's bytes;
+//   upper quarters (g >= 2): their low 4 bits are the nibbles of scales[u+8]
+//   and scales[u+9] (scale: low nibble, min: high nibble; Q gathers the two
+//   bytes twice) and their top 2 bits the top 2 bits of P's bytes.
 struct FieldSel {
-  uint32_t sh;   // 8 * u
-  bool upper;
+  uint32_t psel;   // v_perm selector of P from (scales[4..7] : scales[0..3])
+  uint32_t qsel;   // v_perm selector of Q from (scales[8..11] : P): P itself below
+  uint32_t sh_hi;  // 0 below, 2 above: bits 4-5 (below) or 6-7 (above) of P to 4-5
+  uint32_t sh_m;   // 0 below, 4 above: where the mins' low 4 bits sit in Q
 };
 
-__device__ __forceinline__ void slice_scales(const Slice& s, const FieldSel& f, float& sc0,
-                                             float& sc1, float& mn0, float& mn1) {
-  const float d = half_bits_to_float(s.h & 0xFFFFu);
-  const float dmin = half_bits_to_float(s.h >> 16);
-  const uint32_t a = s.s0 >> f.sh, b = s.s1 >> f.sh, c = s.s2 >> f.sh;
-  uint32_t c0, c1, m0, m1;
-  if (f.upper) {
-    // scale = low nibble of scales[8+u] | top bits of scales[u]; min = high
-    // nibble of scales[8+u] | top bits of scales[4+u]
-    c0 = (c & 15u) | ((a >> 6) & 3u) << 4;
-    c1 = ((c >> 8) & 15u) | ((a >> 14) & 3u) << 4;
-    m0 = ((c >> 4) & 15u) | ((b >> 6) & 3u) << 4;
-    m1 = ((c >> 12) & 15u) | ((b >> 14) & 3u) << 4;
-  } else {
-    c0 = a & 63u;
-    c1 = (a >> 8) & 63u;
-    m0 = b & 63u;
-    m1 = (b >> 8) & 63u;
-  }
-  sc0 = d * static_cast<float>(c0);
-  sc1 = d * static_cast<float>(c1);
-  mn0 = dmin * static_cast<float>(m0);
-  mn1 = dmin * static_cast<float>(m1);
+__device__ __forceinline__ FieldSel field_sel(int g) {
+  const uint32_t u = (2u * static_cast<uint32_t>(g)) & 3u;
+  const bool upper = g >= 2;
+  FieldSel f;
+  f.psel = u | (u + 1u) << 8 | (u + 4u) << 16 | (u + 5u) << 24;
+  f.qsel = upper ? ((u + 4u) | (u + 5u) << 8 | (u + 4u) << 16 | (u + 5u) << 24) : 0x03020100u;
+  f.sh_hi = upper ? 2u : 0u;
+  f.sh_m = upper ? 4u : 0u;
+  return f;
+}
+
+// The four 6-bit fields of a lane's two sub-blocks as bytes [sc0, sc1, m0, m1].
+__device__ __forceinline__ uint32_t slice_fields(const uint4& h, const FieldSel& f) {
+  const uint32_t P = __builtin_amdgcn_perm(h.z, h.y, f.psel);
+  const uint32_t Q = __builtin_amdgcn_perm(h.w, P, f.qsel);
+  const uint32_t lo = (Q & 0x00000F0Fu) | ((Q >> f.sh_m) & 0x0F0F0000u);
+  return lo | ((P >> f.sh_hi) & 0x30303030u);
 }
 
 // A lane's slice of the activations in integer form.
@@ -198,16 +166,22 @@ __device__ __forceinline__ int plane_dot(const uint32_t (&w)[8], int shift, cons
   return static_cast<int>(s0 + (s1 << 8)) + s2 * 65536;
 }
 
-__device__ __forceinline__ float slice_dot(const Slice& s, const FieldSel& f, const XSlice& x) {
-  float sc0, sc1, mn0, mn1;
-  slice_scales(s, f, sc0, sc1, mn0, mn1);
+// The lane's share of a row: sub-blocks 2g (low nibbles) and 2g+1 (high
+// nibbles) against its slice of x,
+//   d * 2^(e-21) * (sc0 * P_lo + sc1 * P_hi) - dmin * (m0 * X0 + m1 * X1).
+// A lane whose loads were out of range (zeros) gives 0.
+__device__ __forceinline__ float slice_dot(const RawSlice& s, const FieldSel& f, const XSlice& x) {
+  const uint32_t F = slice_fields(s.h, f);
+  const float d = half_bits_to_float(s.h.x & 0xFFFFu);
+  const float dmin = half_bits_to_float(s.h.x >> 16);
   const uint32_t w[8] = {s.q0.x, s.q0.y, s.q0.z, s.q0.w, s.q1.x, s.q1.y, s.q1.z, s.q1.w};
   const float lo = static_cast<float>(plane_dot(w, 0, x, 0));  // sub-block 2g: low nibbles
   const float hi = static_cast<float>(plane_dot(w, 4, x, 8));  // sub-block 2g+1: high nibbles
-  float r = fmaf(sc1, hi, sc0 * lo) * x.scale;
-  r = fmaf(-mn0, x.sum0, r);
-  r = fmaf(-mn1, x.sum1, r);
-  return r;
+  const float sc0 = static_cast<float>(F & 0xFFu), sc1 = static_cast<float>((F >> 8) & 0xFFu);
+  const float m0 = static_cast<float>((F >> 16) & 0xFFu), m1 = static_cast<float>(F >> 24);
+  const float qa = fmaf(sc1, hi, sc0 * lo);
+  const float ma = fmaf(m1, x.sum1, m0 * x.sum0);
+  return fmaf(qa, d * x.scale, -(dmin * ma));
 }
 
 // Launch geometry (all per workgroup):
@@ -249,9 +223,9 @@ __device__ __forceinline__ void convert_unit(const float4 (&xr)[4], int u, bool 
     amax = fmaxf(amax, fabsf(v[i]));
     sum += v[i];
   }
-  amax = fmaxf(amax, dpp<0xB1>(amax));
-  amax = fmaxf(amax, dpp<0x4E>(amax));
-  sum += dpp<0xB1>(sum);  // units 0+1 and 2+3: the two 32-value halves
+  amax = fmaxf(amax, dpp_f<0xB1>(amax));
+  amax = fmaxf(amax, dpp_f<0x4E>(amax));
+  sum += dpp_f<0xB1>(sum);  // units 0+1 and 2+3: the two 32-value halves
   // |x| < 2^e over the slice; e >= -105 keeps 2^(21-e) a normal f32 (slices
   // below 2^-106 keep fewer bits), and an all-zero slice takes e = 0
   const int eb = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu);
@@ -299,13 +273,16 @@ template <bool GU, bool BF16, int MODE, int LAYOUT, int XU, int PF>
 __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo geo) {
   constexpr bool WIDE = LAYOUT == kWide;
   constexpr bool SEG64 = LAYOUT != kNarrow;
+  // rows of one or more whole wavefronts reduce their PF (non-GU) or 2 * PF
+  // (GU: gate and up) values per lane together: 4 of them
+  static_assert(!SEG64 || (GU ? 2 * PF : PF) == 4, "one-wave reduction takes four values");
   extern __shared__ __attribute__((aligned(16))) uint32_t smem_u[];
   const int K = a.k >> 8;  // blocks per row
   const int S = 4 * K;     // slices per row
   const int units = 4 * S;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nthr = geo.waves * 64;
   // every argument the weight stream needs, fetched in one batch of scalar
   // loads (otherwise the compiler spreads them over dependent round trips
@@ -313,11 +290,15 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
   asm volatile("" ::"s"(a.w), "s"(a.w_up), "s"(a.x), "s"(a.k), "s"(a.n), "s"(geo.rows), "s"(geo.step),
                "s"(geo.lpr_log), "s"(geo.wslot), "s"(geo.wpart));
 
-  // this lane's row slot (within a step) and slice position
+  // this lane's row slot (within a step) and slice position; for rows of one
+  // or more whole wavefronts the row slot is uniform in the wavefront
   int rslot, slice;
-  if constexpr (!WIDE) {
+  if constexpr (LAYOUT == kNarrow) {
     rslot = wave * geo.rpw + (lane >> geo.lpr_log);
     slice = lane & ((1 << geo.lpr_log) - 1);
+  } else if constexpr (LAYOUT == kOneWave) {
+    rslot = wave;
+    slice = lane;
   } else {
     rslot = static_cast<int>((geo.wslot >> (4 * wave)) & 15u);
     slice = static_cast<int>((geo.wpart >> (4 * wave)) & 15u) * 64 + lane;
@@ -325,9 +306,8 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
   const bool lane_ok = slice < S && rslot < geo.step;
   const int b = lane_ok ? slice >> 2 : 0;
   const int g = lane & 3;  // == slice & 3: S is a multiple of 4 and segments are aligned
-  FieldSel fsel;
-  fsel.sh = 8u * static_cast<uint32_t>((2 * g) & 3);
-  fsel.upper = g >= 2;
+  const FieldSel fsel = field_sel(g);
+  const uint32_t qoff = 16u + 32u * static_cast<uint32_t>(g);
 
   // step it holds rows it*step .. it*step+step-1 of the workgroup; it exists
   // while it*step < rows
@@ -336,20 +316,21 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
   const uint32_t wbytes = static_cast<uint32_t>(rows) * static_cast<uint32_t>(K) * kBlockBytes;
   // Products of uniform values pass through an opaque scalar move: the
   // compiler would otherwise fold them with a lane value into a 64-bit
-  // multiply-add whose (unused) high addend register may be a load still in
+  // multiply-add whose (unused) high addend register may be a load in
   // flight, and wait for it (it sees through readfirstlane of a scalar).
   auto uni = [](int v) -> int {
     int r;
     asm("s_mov_b32 %0, %1" : "=s"(r) : "s"(v));
     return r;
   };
-  // byte offset of this lane's block in step it: base + it * stride (adds
-  // only), kOob past the last row
+  // Byte offset of this lane's block in step it: base + it * stride (adds
+  // only).  Rows past the workgroup's last start at or past the resource's
+  // size and read zeros; a lane past the row's last slice starts at kOob
+  // (2^31).  Every offset stays below 2^32: the workgroup's bytes and the
+  // PF steps past its end stay below 2^31 (make_geo), so nothing wraps and
+  // no load needs a branch or a per-row select.
   const uint32_t stride = static_cast<uint32_t>(geo.step * K) * kBlockBytes;
-  const uint32_t base = static_cast<uint32_t>(rslot * K + b) * kBlockBytes;
-  auto step_off = [&](int it, uint32_t off) -> uint32_t {
-    return lane_ok && rslot < rows - uni(it * geo.step) ? off : kOob;
-  };
+  const uint32_t base = lane_ok ? static_cast<uint32_t>(rslot * K + b) * kBlockBytes : kOob;
   // Unit j of this thread's activation units (XU of them, XU * nthr >= units
   // by construction of the launch).
   auto unit_off = [&](int u, int c) -> uint32_t {
@@ -360,6 +341,20 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
   float* part = reinterpret_cast<float*>(smem_u + x_words(S));                   // [GU?2:1][rows][wr]
   const int seg_mask = SEG64 ? 63 : (1 << geo.lpr_log) - 1;
 
+  // rows of whole wavefronts: which of the four reduced values each lane
+  // ends up holding (row_reduce<4>), and the lanes that hold values 0..3
+  int hold_tok = 0;
+  bool holder = false;
+  int hl[4] = {63, 63, 63, 63};
+  if constexpr (SEG64) {
+    token_map<4>(lane, hold_tok, holder);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint64_t m = __ballot(holder && hold_tok == t);
+      hl[t] = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(m)));
+    }
+  }
+
   // One pass over the workgroup's rows of one matrix for one activation row;
   // writes y row `yrow`.
   auto pass = [&](size_t mofs, int xrow, int yrow) {
@@ -369,6 +364,7 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
     const size_t xel = static_cast<size_t>(xrow) * a.ldx;
     const rsrc_t rx = BF16 ? make_rsrc(static_cast<const uint16_t*>(a.x) + xel, 2u * a.k)
                            : make_rsrc(static_cast<const float*>(a.x) + xel, 4u * a.k);
+    float* yout = a.y + static_cast<size_t>(yrow) * a.ldy + row0;
 
     // 1. this thread's activation units, loaded before any weight
     float4 xr[XU][4];
@@ -381,9 +377,9 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
     RawSlice sg[PF], su[GU ? PF : 1];
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      const uint32_t off = step_off(p, base + static_cast<uint32_t>(uni(p * static_cast<int>(stride))));
-      load_slice(rg, off, g, sg[p]);
-      if constexpr (GU) load_slice(ru, off, g, su[p]);
+      const uint32_t off = base + static_cast<uint32_t>(uni(p * static_cast<int>(stride)));
+      load_slice(rg, off, qoff, sg[p]);
+      if constexpr (GU) load_slice(ru, off, qoff, su[p]);
     }
 
     // 3. activations -> digits in LDS, once per workgroup (the loop bounds are
@@ -414,32 +410,55 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
     }
 
     // 4. row loop: consume step p while steps p+1 .. p+PF-1 are in flight.
-    //    The loads are never under a branch (rows past the end read kOob),
-    //    the last group issues none, and inactive lanes contribute 0 to the
-    //    DPP sums.
-    auto dot = [&](const RawSlice& raw, bool ok) -> float {
-      const float v = slice_dot(expand(raw), fsel, xs);
-      return ok ? v : 0.f;
-    };
+    //    The loads are never under a branch (rows past the end read zeros),
+    //    the last group issues none, and lanes past the row's end give 0.
     auto finish = [&](float (&o)[PF], float (&ou)[PF], int it0) {
+      if constexpr (!SEG64) {
 #pragma unroll
-      for (int p = 0; p < PF; ++p) {
-        o[p] = SEG64 ? segment_sum<64>(o[p]) : segment_sum_rt(o[p], seg_mask + 1);
-        if constexpr (GU) ou[p] = SEG64 ? segment_sum<64>(ou[p]) : segment_sum_rt(ou[p], seg_mask + 1);
-      }
+        for (int p = 0; p < PF; ++p) {
+          o[p] = segment_sum_rt(o[p], seg_mask + 1);
+          if constexpr (GU) ou[p] = segment_sum_rt(ou[p], seg_mask + 1);
+        }
 #pragma unroll
-      for (int p = 0; p < PF; ++p) {
-        const int r = uni((it0 + p) * geo.step) + rslot;
-        // the segment's last lane holds the row sum (it may be a padding lane)
-        if (rslot < geo.step && r < rows && (lane & seg_mask) == seg_mask) {
-          if constexpr (!WIDE) {
+        for (int p = 0; p < PF; ++p) {
+          const int r = uni((it0 + p) * geo.step) + rslot;
+          // the segment's last lane holds the row sum (it may be a padding lane)
+          if (rslot < geo.step && r < rows && (lane & seg_mask) == seg_mask) {
             float out = o[p];
             if constexpr (GU) out = silu_mul(o[p], ou[p]);
-            a.y[static_cast<size_t>(yrow) * a.ldy + row0 + r] = out;
-          } else {
-            part[r * geo.wr + (slice >> 6)] = o[p];
-            if constexpr (GU) part[(rows + r) * geo.wr + (slice >> 6)] = ou[p];
+            yout[r] = out;
           }
+        }
+      } else {
+        // four values per lane -> four totals (row_reduce<4>): non-GU the
+        // PF = 4 steps' rows, GU the two steps' gate and up rows
+        float v[4];
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+          v[p] = o[p];
+          if constexpr (GU) v[PF + p] = ou[p];
+        }
+        const float tot = row_reduce<4>(v, lane);
+        if constexpr (!GU) {
+          const int r = uni(it0 * geo.step) + hold_tok * geo.step + rslot;
+          if (holder && r < rows) {
+            if constexpr (!WIDE) yout[r] = tot;
+            else part[r * geo.wr + (slice >> 6)] = tot;
+          }
+        } else if constexpr (!WIDE) {
+          // gate totals of steps it0, it0 + 1 and the up totals, uniform
+          const float t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), hl[0]));
+          const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), hl[1]));
+          const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), hl[2]));
+          const float t3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), hl[3]));
+          const int r0 = uni(it0 * geo.step) + rslot;
+          const int r1 = r0 + geo.step;
+          if (lane == 0 && r0 < rows) yout[r0] = silu_mul(t0, t2);
+          if (lane == 1 && r1 < rows) yout[r1] = silu_mul(t1, t3);
+        } else {
+          const int p = hold_tok & 1;
+          const int r = uni(it0 * geo.step) + p * geo.step + rslot;
+          if (holder && r < rows) part[((hold_tok >> 1) * rows + r) * geo.wr + (slice >> 6)] = tot;
         }
       }
     };
@@ -449,13 +468,12 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
       float o[PF], ou[PF];
 #pragma unroll
       for (int p = 0; p < PF; ++p) {
-        const bool ok = lane_ok && rslot < rows - uni((it0 + p) * geo.step);
-        o[p] = dot(sg[p], ok);
+        o[p] = slice_dot(sg[p], fsel, xs);
         ou[p] = 0.f;
-        if constexpr (GU) ou[p] = dot(su[p], ok);
-        const uint32_t off = step_off(it0 + p + PF, next + static_cast<uint32_t>(uni(p * static_cast<int>(stride))));
-        load_slice(rg, off, g, sg[p]);
-        if constexpr (GU) load_slice(ru, off, g, su[p]);
+        if constexpr (GU) ou[p] = slice_dot(su[p], fsel, xs);
+        const uint32_t off = next + static_cast<uint32_t>(uni(p * static_cast<int>(stride)));
+        load_slice(rg, off, qoff, sg[p]);
+        if constexpr (GU) load_slice(ru, off, qoff, su[p]);
       }
       finish(o, ou, it0);
     }
@@ -466,9 +484,8 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
         o[p] = 0.f;
         ou[p] = 0.f;
         if ((it0 + p) * geo.step < rows) {  // uniform
-          const bool ok = lane_ok && rslot < rows - uni((it0 + p) * geo.step);
-          o[p] = dot(sg[p], ok);
-          if constexpr (GU) ou[p] = dot(su[p], ok);
+          o[p] = slice_dot(sg[p], fsel, xs);
+          if constexpr (GU) ou[p] = slice_dot(su[p], fsel, xs);
         }
       }
       finish(o, ou, it0);
@@ -484,7 +501,7 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
         }
         float out = s;
         if constexpr (GU) out = silu_mul(s, su_);
-        a.y[static_cast<size_t>(yrow) * a.ldy + row0 + r] = out;
+        yout[r] = out;
       }
     }
   };
@@ -533,9 +550,8 @@ __global__ __launch_bounds__(kThreadsMax) void moe_down_kernel(GemvArgs a, Geo g
   const bool lane_ok = slice < S;
   const int b = lane_ok ? slice >> 2 : 0;
   const int g = lane & 3;
-  FieldSel fsel;
-  fsel.sh = 8u * static_cast<uint32_t>((2 * g) & 3);
-  fsel.upper = g >= 2;
+  const FieldSel fsel = field_sel(g);
+  const uint32_t qoff = 16u + 32u * static_cast<uint32_t>(g);
   const int seg_mask = SEG64 ? 63 : (1 << geo.lpr_log) - 1;
   const int step = geo.rpw;  // rows per wavefront step
   auto uni = [](int v) -> int {
@@ -543,11 +559,10 @@ __global__ __launch_bounds__(kThreadsMax) void moe_down_kernel(GemvArgs a, Geo g
     asm("s_mov_b32 %0, %1" : "=s"(r) : "s"(v));
     return r;
   };
+  // as in gemv_d4_kernel: rows past the end read zeros through the resource
+  // size, lanes past the row's end start at kOob
   const uint32_t stride = static_cast<uint32_t>(step * K) * kBlockBytes;
-  const uint32_t base = static_cast<uint32_t>(rslot * K + b) * kBlockBytes;
-  auto step_off = [&](int it, uint32_t off) -> uint32_t {
-    return lane_ok && rslot < rows - uni(it * step) ? off : kOob;
-  };
+  const uint32_t base = lane_ok ? static_cast<uint32_t>(rslot * K + b) * kBlockBytes : kOob;
 
   for (int sl = wave; sl < a.top_k; sl += geo.waves) {  // uniform in the wavefront
     const int pr = t * a.top_k + sl;
@@ -568,7 +583,7 @@ __global__ __launch_bounds__(kThreadsMax) void moe_down_kernel(GemvArgs a, Geo g
     RawSlice sg[PF];
 #pragma unroll
     for (int p = 0; p < PF; ++p)
-      load_slice(rg, step_off(p, base + static_cast<uint32_t>(uni(p * static_cast<int>(stride)))), g, sg[p]);
+      load_slice(rg, base + static_cast<uint32_t>(uni(p * static_cast<int>(stride))), qoff, sg[p]);
     // 2. digits of h row pr in this wavefront's LDS (the wavefront's own
     //    writes: complete at lgkmcnt(0))
 #pragma unroll
@@ -603,18 +618,14 @@ __global__ __launch_bounds__(kThreadsMax) void moe_down_kernel(GemvArgs a, Geo g
         if (r < rows && (lane & seg_mask) == seg_mask) rs[r] = o[p];
       }
     };
-    auto dot = [&](const RawSlice& raw, bool ok) -> float {
-      const float v = slice_dot(expand(raw), fsel, xs);
-      return ok ? v : 0.f;
-    };
     int it0 = 0;
     uint32_t next = base + PF * stride;
     for (; (it0 + PF) * step < rows; it0 += PF, next += PF * stride) {
       float o[PF];
 #pragma unroll
       for (int p = 0; p < PF; ++p) {
-        o[p] = dot(sg[p], lane_ok && rslot < rows - uni((it0 + p) * step));
-        load_slice(rg, step_off(it0 + p + PF, next + static_cast<uint32_t>(uni(p * static_cast<int>(stride)))), g, sg[p]);
+        o[p] = slice_dot(sg[p], fsel, xs);
+        load_slice(rg, next + static_cast<uint32_t>(uni(p * static_cast<int>(stride))), qoff, sg[p]);
       }
       finish(o, it0);
     }
@@ -623,7 +634,7 @@ __global__ __launch_bounds__(kThreadsMax) void moe_down_kernel(GemvArgs a, Geo g
 #pragma unroll
       for (int p = 0; p < PF; ++p) {
         o[p] = 0.f;
-        if ((it0 + p) * step < rows) o[p] = dot(sg[p], lane_ok && rslot < rows - uni((it0 + p) * step));
+        if ((it0 + p) * step < rows) o[p] = slice_dot(sg[p], fsel, xs);
       }
       finish(o, it0);
     }
@@ -688,7 +699,10 @@ Geo make_geo(int n, int k, int slots, bool gu, int mode) {
   // MoE pairs: one prefetch group per workgroup (no serial memory round
   // trips; the many pairs fill the chip)
   if (mode == kPair && g.rows > pf * g.step) g.rows = pf * g.step;
-  const int cap_bytes = static_cast<int>((static_cast<size_t>(kOob) - 1) / (static_cast<size_t>(K) * kBlockBytes)) /
+  // a workgroup's bytes stay below 2^30, so that its offsets, the PF steps
+  // issued past its last row and the kOob start of lanes past the row's end
+  // all stay below 2^32
+  const int cap_bytes = static_cast<int>(((size_t{1} << 30) - 1) / (static_cast<size_t>(K) * kBlockBytes)) /
                         g.step * g.step;
   if (g.rows > cap_bytes) g.rows = cap_bytes;
   // (per row: the partials of a row that spans wavefronts)
