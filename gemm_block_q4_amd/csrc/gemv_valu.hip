@@ -51,9 +51,10 @@ namespace q4k {
 
 namespace {
 
-constexpr int kThreadsMax = 512;
+constexpr int kThreadsMax = 768;  // the wide layout: 12 wavefronts
+constexpr int kThreadsNarrow = 512;
 constexpr int kWavesNarrow = 4;  // wavefronts per workgroup when a row fits one wavefront
-constexpr int kWavesWide = 8;    // at most this many when a row spans wavefronts
+constexpr int kWavesWide = 12;   // at most this many when a row spans wavefronts
 constexpr size_t kLdsMax = 160 * 1024;
 
 // Four activations at element offset `off` of a buffer (kOob: zeros).
@@ -191,26 +192,49 @@ __device__ __forceinline__ float slice_dot(const RawSlice& s, const FieldSel& f,
 //   rpw  = rows per wavefront per step (64 / lpr when wr == 1, else 1);
 //   step = rows per workgroup per step; rows = rows per workgroup.
 // The kernel divides by none of them: lpr_log = log2(lpr) when wr == 1, and
-// for wr > 1 nibble w of wslot / wpart holds w / wr and w % wr.
+// for wr > 1 nibble w of wslot / wpart holds w / wr and w % wr (up to 12
+// wavefronts).
 struct Geo {
   int lpr, wr, rpw, waves, step, rows;
   int lpr_log;
-  uint32_t wslot, wpart;
+  uint64_t wslot, wpart;
 };
 
 // Row layouts: rows narrower than a wavefront (segments of lpr lanes), rows of
 // exactly one wavefront, rows spanning wavefronts.
 enum Layout { kNarrow = 0, kOneWave = 1, kWide = 2 };
 
-// LDS words: digit planes [S][48] and slice info [S][4] (scale, sum0, sum1,
-// unused), then the row partials when a row spans wavefronts.
-__host__ __device__ __forceinline__ size_t x_words(int slices) { return static_cast<size_t>(slices) * 52; }
+// LDS words: the digits as twelve planes (plane 4d + j holds words 4j .. 4j+3
+// of digit plane d of every slice, 16 bytes per slice, so that the lanes of
+// a wavefront read consecutive 16-byte words without bank conflicts; each
+// plane is padded by 16 bytes so that the four writers of a slice hit
+// different banks), then the slice info [S][4] (scale, sum0, sum1, unused),
+// then the row partials when a row spans wavefronts.
+__host__ __device__ __forceinline__ size_t dig_plane_words(int slices) { return 4 * static_cast<size_t>(slices) + 4; }
+__host__ __device__ __forceinline__ size_t xinfo_offset(int slices) { return 12 * dig_plane_words(slices); }
+__host__ __device__ __forceinline__ size_t x_words(int slices) {
+  return xinfo_offset(slices) + 4 * static_cast<size_t>(slices);
+}
+
+// The lane's slice of the digits from LDS.
+__device__ __forceinline__ void read_digits(const uint32_t* __restrict__ dig, int S, int slice,
+                                            uint32_t (&dg)[3][16]) {
+  const size_t ps = dig_plane_words(S);
+#pragma unroll
+  for (int d = 0; d < 3; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 t4 = *reinterpret_cast<const uint4*>(dig + (4 * d + i) * ps + 4 * static_cast<size_t>(slice));
+      dg[d][4 * i] = t4.x; dg[d][4 * i + 1] = t4.y;
+      dg[d][4 * i + 2] = t4.z; dg[d][4 * i + 3] = t4.w;
+    }
+}
 
 // Converts one 16-value activation unit u (values 16u .. 16u+15, quarter u & 3
 // of slice u >> 2) to byte planes in LDS.  The four units of a slice are an
 // aligned lane quad, so the slice maximum and the half sums are quad DPP
 // reductions; every lane of the quad must execute this (uniform control flow).
-__device__ __forceinline__ void convert_unit(const float4 (&xr)[4], int u, bool valid,
+__device__ __forceinline__ void convert_unit(const float4 (&xr)[4], int u, bool valid, int S,
                                              uint32_t* __restrict__ dig, float* __restrict__ xinfo) {
   float v[16];
 #pragma unroll
@@ -248,10 +272,11 @@ __device__ __forceinline__ void convert_unit(const float4 (&xr)[4], int u, bool 
     p2[q] = (h + 0x40404040u) ^ 0x80808080u;  // bytewise u2 - 64 (no carries: u2 + 64 < 256)
   }
   const int s = u >> 2, qq = u & 3;
-  uint32_t* base = dig + static_cast<size_t>(s) * 48 + 4 * qq;
+  const size_t ps = dig_plane_words(S);
+  uint32_t* base = dig + qq * ps + 4 * static_cast<size_t>(s);
   *reinterpret_cast<uint4*>(base) = make_uint4(p0[0], p0[1], p0[2], p0[3]);
-  *reinterpret_cast<uint4*>(base + 16) = make_uint4(p1[0], p1[1], p1[2], p1[3]);
-  *reinterpret_cast<uint4*>(base + 32) = make_uint4(p2[0], p2[1], p2[2], p2[3]);
+  *reinterpret_cast<uint4*>(base + 4 * ps) = make_uint4(p1[0], p1[1], p1[2], p1[3]);
+  *reinterpret_cast<uint4*>(base + 8 * ps) = make_uint4(p2[0], p2[1], p2[2], p2[3]);
   if (qq == 0) {
     // amax - amax is 0 for a finite maximum and NaN otherwise
     xinfo[4 * s] = __uint_as_float(static_cast<uint32_t>(127 - 21 + e) << 23) + (amax - amax);
@@ -270,12 +295,13 @@ __device__ __forceinline__ void convert_unit(const float4 (&xr)[4], int u, bool 
 enum Mode { kDense = 0, kPair = 1 };
 
 template <bool GU, bool BF16, int MODE, int LAYOUT, int XU, int PF>
-__global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo geo) {
+__global__ __launch_bounds__(LAYOUT == kWide ? kThreadsMax : kThreadsNarrow) void gemv_d4_kernel(GemvArgs a, Geo geo) {
   constexpr bool WIDE = LAYOUT == kWide;
   constexpr bool SEG64 = LAYOUT != kNarrow;
   // rows of one or more whole wavefronts reduce their PF (non-GU) or 2 * PF
-  // (GU: gate and up) values per lane together: 4 of them
-  static_assert(!SEG64 || (GU ? 2 * PF : PF) == 4, "one-wave reduction takes four values");
+  // (GU: gate and up) values per lane together: 4 or 8 of them
+  constexpr int NV = GU ? 2 * PF : PF;
+  static_assert(!SEG64 || NV == 2 || NV == 4 || NV == 8, "one-wave reduction takes two, four or eight values");
   extern __shared__ __attribute__((aligned(16))) uint32_t smem_u[];
   const int K = a.k >> 8;  // blocks per row
   const int S = 4 * K;     // slices per row
@@ -336,20 +362,22 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
   auto unit_off = [&](int u, int c) -> uint32_t {
     return u < units ? static_cast<uint32_t>(16 * u + 4 * c) : kOob;
   };
-  uint32_t* dig = smem_u;                                                         // [S][48]
-  float* xinfo = reinterpret_cast<float*>(smem_u + static_cast<size_t>(S) * 48);  // [S][4]
+  uint32_t* dig = smem_u;                                                    // 12 planes
+  float* xinfo = reinterpret_cast<float*>(smem_u + xinfo_offset(S));          // [S][4]
   float* part = reinterpret_cast<float*>(smem_u + x_words(S));                   // [GU?2:1][rows][wr]
   const int seg_mask = SEG64 ? 63 : (1 << geo.lpr_log) - 1;
 
-  // rows of whole wavefronts: which of the four reduced values each lane
-  // ends up holding (row_reduce<4>), and the lanes that hold values 0..3
+  // rows of whole wavefronts: which of the NV reduced values each lane ends
+  // up holding (row_reduce<NV>), and the lanes that hold values 0 .. NV-1
   int hold_tok = 0;
   bool holder = false;
-  int hl[4] = {63, 63, 63, 63};
-  if constexpr (SEG64) {
-    token_map<4>(lane, hold_tok, holder);
+  int hl[NV];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < NV; ++t) hl[t] = 63;
+  if constexpr (SEG64) {
+    token_map<NV>(lane, hold_tok, holder);
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
       const uint64_t m = __ballot(holder && hold_tok == t);
       hl[t] = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(m)));
     }
@@ -373,6 +401,14 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
 #pragma unroll
       for (int c = 0; c < 4; ++c) xr[j][c] = load_x4<BF16>(rx, unit_off(tid + j * nthr, c));
 
+    // Every wavefront issues its activation loads before any weight load:
+    // the compute unit's texture path (64 B/clk) serves loads roughly in
+    // issue order, and the activations, needed first, would otherwise queue
+    // behind other wavefronts' weight loads (0.3 us on 4096 x 4096).
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
     // 2. weight loads of the first PF steps
     RawSlice sg[PF], su[GU ? PF : 1];
 #pragma unroll
@@ -387,7 +423,7 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
 #pragma unroll
     for (int j = 0; j < XU; ++j) {
       const int u = tid + j * nthr;
-      convert_unit(xr[j], u, u < units, dig, xinfo);
+      convert_unit(xr[j], u, u < units, S, dig, xinfo);
     }
     // A barrier without a memory fence: the digits are LDS writes, complete
     // at lgkmcnt(0), and a fence would also wait for the weight loads in
@@ -396,15 +432,7 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
     __builtin_amdgcn_s_barrier();
     XSlice xs;
     {
-      const uint32_t* dbase = dig + static_cast<size_t>(lane_ok ? slice : 0) * 48;
-#pragma unroll
-      for (int d = 0; d < 3; ++d)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint4 t4 = *reinterpret_cast<const uint4*>(dbase + 16 * d + 4 * i);
-          xs.dg[d][4 * i] = t4.x; xs.dg[d][4 * i + 1] = t4.y;
-          xs.dg[d][4 * i + 2] = t4.z; xs.dg[d][4 * i + 3] = t4.w;
-        }
+      read_digits(dig, S, lane_ok ? slice : 0, xs.dg);
       const float4 inf = *reinterpret_cast<const float4*>(xinfo + 4 * (lane_ok ? slice : 0));
       xs.scale = inf.x; xs.sum0 = inf.y; xs.sum1 = inf.z;
     }
@@ -430,15 +458,15 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
           }
         }
       } else {
-        // four values per lane -> four totals (row_reduce<4>): non-GU the
-        // PF = 4 steps' rows, GU the two steps' gate and up rows
-        float v[4];
+        // NV values per lane -> NV totals (row_reduce<NV>): non-GU the PF
+        // steps' rows, GU the PF steps' gate rows, then their up rows
+        float v[NV];
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
           v[p] = o[p];
           if constexpr (GU) v[PF + p] = ou[p];
         }
-        const float tot = row_reduce<4>(v, lane);
+        const float tot = row_reduce<NV>(v, lane);
         if constexpr (!GU) {
           const int r = uni(it0 * geo.step) + hold_tok * geo.step + rslot;
           if (holder && r < rows) {
@@ -446,19 +474,22 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
             else part[r * geo.wr + (slice >> 6)] = tot;
           }
         } else if constexpr (!WIDE) {
-          // gate totals of steps it0, it0 + 1 and the up totals, uniform
-          const float t0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), hl[0]));
-          const float t1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), hl[1]));
-          const float t2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), hl[2]));
-          const float t3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), hl[3]));
-          const int r0 = uni(it0 * geo.step) + rslot;
-          const int r1 = r0 + geo.step;
-          if (lane == 0 && r0 < rows) yout[r0] = silu_mul(t0, t2);
-          if (lane == 1 && r1 < rows) yout[r1] = silu_mul(t1, t3);
+          // lane p (< PF) gathers the gate and up totals of step it0 + p
+          // from their holders (uniform lane indices) and stores silu * up
+          float gt = 0.f, ut = 0.f;
+#pragma unroll
+          for (int p = 0; p < PF; ++p) {
+            const float g_p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), hl[p]));
+            const float u_p = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tot), hl[PF + p]));
+            gt = lane == p ? g_p : gt;
+            ut = lane == p ? u_p : ut;
+          }
+          const int r = uni(it0 * geo.step) + lane * geo.step + rslot;
+          if (lane < PF && r < rows) yout[r] = silu_mul(gt, ut);
         } else {
-          const int p = hold_tok & 1;
+          const int p = hold_tok % PF;
           const int r = uni(it0 * geo.step) + p * geo.step + rslot;
-          if (holder && r < rows) part[((hold_tok >> 1) * rows + r) * geo.wr + (slice >> 6)] = tot;
+          if (holder && r < rows) part[((hold_tok / PF) * rows + r) * geo.wr + (slice >> 6)] = tot;
         }
       }
     };
@@ -524,7 +555,7 @@ __global__ __launch_bounds__(kThreadsMax) void gemv_d4_kernel(GemvArgs a, Geo ge
 // row adds wts[p] * res[s][row] over the valid slots in slot order
 // (deterministic) and writes y[t][row].  No pair buffer and no combine pass.
 template <int LAYOUT, int XU>
-__global__ __launch_bounds__(kThreadsMax) void moe_down_kernel(GemvArgs a, Geo geo) {
+__global__ __launch_bounds__(kThreadsNarrow) void moe_down_kernel(GemvArgs a, Geo geo) {
   constexpr bool SEG64 = LAYOUT != kNarrow;
   constexpr int PF = 4;
   extern __shared__ __attribute__((aligned(16))) uint32_t smem_u[];
@@ -542,7 +573,7 @@ __global__ __launch_bounds__(kThreadsMax) void moe_down_kernel(GemvArgs a, Geo g
 
   // per-wavefront digits, then res[top_k][geo.rows]
   uint32_t* dig = smem_u + static_cast<size_t>(wave) * x_words(S);
-  float* xinfo = reinterpret_cast<float*>(dig + static_cast<size_t>(S) * 48);
+  float* xinfo = reinterpret_cast<float*>(dig + xinfo_offset(S));
   float* res = reinterpret_cast<float*>(smem_u + static_cast<size_t>(geo.waves) * x_words(S));
 
   const int rslot = lane >> geo.lpr_log;  // row within a step (geo.rpw rows per step)
@@ -589,21 +620,13 @@ __global__ __launch_bounds__(kThreadsMax) void moe_down_kernel(GemvArgs a, Geo g
 #pragma unroll
     for (int j = 0; j < XU; ++j) {
       const int u = lane + 64 * j;
-      convert_unit(xr[j], u, u < units, dig, xinfo);
+      convert_unit(xr[j], u, u < units, S, dig, xinfo);
     }
     __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
     XSlice xs;
     {
-      const uint32_t* dbase = dig + static_cast<size_t>(lane_ok ? slice : 0) * 48;
-#pragma unroll
-      for (int d = 0; d < 3; ++d)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint4 t4 = *reinterpret_cast<const uint4*>(dbase + 16 * d + 4 * i);
-          xs.dg[d][4 * i] = t4.x; xs.dg[d][4 * i + 1] = t4.y;
-          xs.dg[d][4 * i + 2] = t4.z; xs.dg[d][4 * i + 3] = t4.w;
-        }
+      read_digits(dig, S, lane_ok ? slice : 0, xs.dg);
       const float4 inf = *reinterpret_cast<const float4*>(xinfo + 4 * (lane_ok ? slice : 0));
       xs.scale = inf.x; xs.sum0 = inf.y; xs.sum1 = inf.z;
     }
@@ -664,7 +687,6 @@ size_t lds_bytes(const Geo& geo, int k, bool gu) {
 }
 
 Geo make_geo(int n, int k, int slots, bool gu, int mode) {
-  const int pf = gu ? 2 : 4;  // steps in flight per wavefront
   Geo g{};
   const int K = k / kQK;
   const int l = 4 * K;
@@ -685,9 +707,9 @@ Geo make_geo(int n, int k, int slots, bool gu, int mode) {
     g.rpw = 1;
     g.waves = g.wr * (g.wr >= kWavesWide ? 1 : kWavesWide / g.wr);  // whole rows
     g.step = g.waves / g.wr;
-    for (int w = 0; w < g.waves; ++w) {  // waves <= 8: one nibble each
-      g.wslot |= static_cast<uint32_t>(w / g.wr) << (4 * w);
-      g.wpart |= static_cast<uint32_t>(w % g.wr) << (4 * w);
+    for (int w = 0; w < g.waves; ++w) {  // waves <= 12: one nibble each
+      g.wslot |= static_cast<uint64_t>(w / g.wr) << (4 * w);
+      g.wpart |= static_cast<uint64_t>(w % g.wr) << (4 * w);
     }
   }
   // rows per workgroup: about 256 workgroups over all slots, whole steps,
@@ -697,7 +719,8 @@ Geo make_geo(int n, int k, int slots, bool gu, int mode) {
   if (want < g.step) want = g.step;
   g.rows = static_cast<int>((want + g.step - 1) / g.step * g.step);
   // MoE pairs: one prefetch group per workgroup (no serial memory round
-  // trips; the many pairs fill the chip)
+  // trips; the many pairs fill the chip); the kernel's steps in flight
+  const int pf = g.wr > 1 ? (gu ? 1 : 2) : (gu ? 2 : 4);
   if (mode == kPair && g.rows > pf * g.step) g.rows = pf * g.step;
   // a workgroup's bytes stay below 2^30, so that its offsets, the PF steps
   // issued past its last row and the kOob start of lanes past the row's end
@@ -717,7 +740,10 @@ Geo make_geo(int n, int k, int slots, bool gu, int mode) {
 
 template <bool GU, bool BF16, int MODE, int LAYOUT, int XU>
 hipError_t launch_layout(const GemvArgs& a, const Geo& geo, size_t lds, int grid_y, hipStream_t stream) {
-  constexpr int PF = GU ? 2 : 4;
+  // steps in flight per wavefront: 4 rows (two of gate and of up), 2 (one
+  // of each) when a row spans wavefronts: 12 wavefronts then keep about as
+  // many bytes in flight per compute unit as 4 wavefronts of whole rows
+  constexpr int PF = LAYOUT == kWide ? (GU ? 1 : 2) : (GU ? 2 : 4);
   auto kern = gemv_d4_kernel<GU, BF16, MODE, LAYOUT, XU, PF>;
   const hipError_t e = lds_opt_in(reinterpret_cast<const void*>(kern), lds);
   if (e != hipSuccess) return e;
