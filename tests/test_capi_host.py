@@ -141,6 +141,9 @@ def test_workspace_sizes(lib):
     pre = w(512, 5120, 17408, 0, 0)
     assert pre >= 512 * (5120 + 5120 // 32 * 4 + 17408 * 4 + 17408 + 17408 // 32 * 4)
     assert w(4, 2048, 768, 8, 0) >= 32 * (768 + 2048) * 4
+    # MoE rows wider than a wavefront (no expert-major combine counters)
+    assert w(2, 512, 4608, 2, 0) >= 4 * (4608 + 512) * 4
+    assert w(2, 8192, 512, 2, 0) >= 4 * (512 + 8192) * 4
     assert w(0, 256, 256, 0, 0) == 0
     assert w(9, 256, 256, 0, 1) == 0      # decode regime caps m at 8
     assert w(4, 256, 256, 2, 2) == 0      # MoE is decode-only
