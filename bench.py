@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5033.0        # dense int8 MFMA: 256 CU x 2.4 GHz x 8192 ops/clk
+FP8_PEAK_TFLOPS = 5033.0       # dense FP8 MFMA: the same 8192 flop/clk per compute unit
 ROTATE_BYTES = 1 << 30         # per rotated tensor set
 
 # HBM bytes of one sweep (the three GEMV launches), measured with rocprofv3 FETCH_SIZE and
@@ -375,6 +376,48 @@ def moe_ffn(q4k, synth, reps=40):
                 weight_gbs=round(distinct * per_expert / (us * 1e-6) / 1e9, 1))
 
 
+def fp8_recipe(q4k, synth, reps=6):
+    """Per-row FP8 recipe on the prefill FFN's projection shapes (gate/up
+    [17408, 5120] and down [5120, 17408]) at 512 and 2048 tokens: the
+    activation quantiser (row absmax + E4M3 codes, f32 x) and the FP8 GEMM
+    with the outer dequant (f32 y), weights quantised once beforehand.
+    Average launch times over graphs of launches on rotated weight copies;
+    GEMM TFLOP/s against the dense FP8 matrix-core peak."""
+    import torch
+    out = {}
+    for n, k, name in ((17408, 5120, "gate_up"), (5120, 17408, "down")):
+        _, w = synth.fp8_case(1, n, k, sub=n)
+        wd = torch.from_numpy(w).cuda()
+        wam = torch.empty(n, dtype=torch.float32, device="cuda")
+        qw = torch.empty((n, k), dtype=torch.uint8, device="cuda")
+        q4k.fp8_absmax_rows(wd, n, k, wam)
+        q4k.fp8_quantize_rows(wd, n, k, wam, qw)
+        del wd
+        copies = [qw] + [qw.clone() for _ in range(3)]
+        for m in (512, 2048):
+            x = torch.from_numpy(synth.fp8_case(m, 1, k, sub=m)[0]).cuda()
+            am = torch.empty(m, dtype=torch.float32, device="cuda")
+            qa = torch.empty((m, k), dtype=torch.uint8, device="cuda")
+            y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+
+            def quant(i):
+                q4k.fp8_absmax_rows(x, m, k, am)
+                q4k.fp8_quantize_rows(x, m, k, am, qa)
+
+            def gemm(i):
+                q4k.fp8_gemm_dequant(qa, am, copies[i % len(copies)], wam, y, m, n, k)
+
+            quant(0)
+            q_us, _, _ = median_us(quant, 4 * reps)
+            g_us, g_min, g_max = median_us(gemm, 4 * reps)
+            tflops = 2.0 * m * n * k / (g_us * 1e-6) / 1e12
+            out[f"{name}_m{m}"] = dict(quantize_us=round(q_us, 1), gemm_us=round(g_us, 1),
+                                       gemm_us_min=round(g_min, 1), gemm_us_max=round(g_max, 1),
+                                       gemm_tflops=round(tflops, 1),
+                                       frac_fp8_peak=round(tflops / FP8_PEAK_TFLOPS, 4))
+    return out
+
+
 # -- CPU oracle baseline ---------------------------------------------------------------
 
 def cpu_info():
@@ -503,6 +546,8 @@ def main():
         secondary["mmq_store_5120_17408_m2048"] = mmq_store(q4k, synth)
         log("bench: Q6_K LM head GEMV")
         secondary["lm_head_q6k_32000_4096"] = lm_head_q6k(q4k, synth)
+        log("bench: per-row FP8 recipe")
+        secondary["fp8_recipe_5120_17408"] = fp8_recipe(q4k, synth)
 
     cpu = None
     if not args.skip_cpu:

@@ -18,6 +18,9 @@ from ._binding import (  # noqa: F401
     ffn_swiglu_q4k,
     ffn_swiglu_q4k_noalloc,
     ffn_swiglu_q4k_workspace_bytes,
+    fp8_absmax_rows,
+    fp8_gemm_dequant,
+    fp8_quantize_rows,
     library_path,
     load_library,
     q4k_gemv,

@@ -51,17 +51,28 @@ _SIGNATURES = {
     "q4k_test_read": (_I, [_VP, _SZ, _VP, _VP]),
     "ffn_swiglu_q4k_noalloc": (_I, [_VP, _VP, _VP, _I, _VP, _I, _I, _I, _I, _VP, _VP, _I, _I, _VP,
                                     _VP]),
+    "fp8_absmax_rows": (_I, [_VP, _I, _I, _VP, _VP]),
+    "fp8_quantize_rows": (_I, [_VP, _I, _I, _VP, _VP, _VP]),
+    "fp8_gemm_dequant": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _VP]),
 }
 
 #: Bytes of the fixed per-device scratch buffer of ffn_swiglu_q4k_noalloc.
 Q4K_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 
-def load_library(path: str | None = None) -> ctypes.CDLL:
-    """Load ``libq4k.so`` once; raise if it has not been built."""
+def load_library(path: str | None = None, share_torch_runtime: bool = True) -> ctypes.CDLL:
+    """Load ``libq4k.so`` once; raise if it has not been built.
+
+    torch is imported first, so that the library's HIP runtime dependency
+    binds to the runtime torch already loaded: loaded the other way round, the
+    process would hold two HIP runtimes, and the library would not know
+    torch's streams or devices.  ``share_torch_runtime=False`` (host-only
+    checks of the argument validation) skips that import."""
     global _LIB
     if _LIB is not None:
         return _LIB
+    if share_torch_runtime:
+        import torch  # noqa: F401
     path = path or library_path()
     if not os.path.exists(path):
         raise Q4KError(-1, f"HIP library not built: {path} is missing "
@@ -254,3 +265,31 @@ def q4k_test_read(buf, nbytes: int, sink, stream=None) -> None:
     """Plain read of the first ``nbytes`` bytes of ``buf`` (read-ceiling hook)."""
     pb, ps = _ptrs((buf, nbytes, None, "buf"), (sink, 4, _I32, "sink"))
     _check(load_library().q4k_test_read(pb, nbytes, ps, _stream(stream)))
+
+
+# -- per-row FP8 (E4M3) recipe ---------------------------------------------------
+
+def fp8_absmax_rows(x, rows: int, cols: int, absmax, stream=None) -> None:
+    """absmax[rows] = max |x[r, :]| of an f32 matrix."""
+    ok = _pos(rows, cols)
+    px, pa = _ptrs((x, 4 * rows * cols if ok else 0, _F32, "x"),
+                   (absmax, 4 * rows if ok else 0, _F32, "absmax"))
+    _check(load_library().fp8_absmax_rows(px, rows, cols, pa, _stream(stream)))
+
+
+def fp8_quantize_rows(x, rows: int, cols: int, absmax, q, stream=None) -> None:
+    """q[rows, cols] = E4M3 codes of x times 448/absmax of its row."""
+    ok = _pos(rows, cols)
+    px, pa, pq = _ptrs((x, 4 * rows * cols if ok else 0, _F32, "x"),
+                       (absmax, 4 * rows if ok else 0, _F32, "absmax"),
+                       (q, rows * cols if ok else 0, _BYTES, "q"))
+    _check(load_library().fp8_quantize_rows(px, rows, cols, pa, pq, _stream(stream)))
+
+
+def fp8_gemm_dequant(a, a_absmax, w, w_absmax, y, m: int, n: int, k: int, stream=None) -> None:
+    """y[m, n] = bf16(A_fp8 @ W_fp8^T) * (a_absmax/448) * (w_absmax/448)."""
+    ok = _pos(m, n, k)
+    p = _ptrs((a, m * k if ok else 0, _BYTES, "a"), (a_absmax, 4 * m if ok else 0, _F32, "a_absmax"),
+              (w, n * k if ok else 0, _BYTES, "w"), (w_absmax, 4 * n if ok else 0, _F32, "w_absmax"),
+              (y, 4 * m * n if ok else 0, _F32, "y"))
+    _check(load_library().fp8_gemm_dequant(*p, m, n, k, _stream(stream)))

@@ -336,6 +336,47 @@ int q4k_test_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
   return launch_status(launch_read_ceiling(buf, bytes, sink, static_cast<hipStream_t>(stream)));
 }
 
+int fp8_absmax_rows(const float* x, int rows, int cols, float* absmax, void* stream) {
+  if (!x || !absmax) return Q4K_ERR_NULL;
+  if (rows < 1 || cols < 1) return Q4K_ERR_SHAPE;
+  size_t e;
+  if (!mul_ok(static_cast<size_t>(rows), static_cast<size_t>(cols), &e)) return Q4K_ERR_OVERFLOW;
+  if (!aligned(x, 4) || !aligned(absmax, 4)) return Q4K_ERR_ALIGN;
+  const int st = check_device();
+  if (st) return st;
+  return launch_status(launch_fp8_absmax_rows(x, rows, cols, absmax, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_quantize_rows(const float* x, int rows, int cols, const float* absmax, uint8_t* q, void* stream) {
+  if (!x || !absmax || !q) return Q4K_ERR_NULL;
+  if (rows < 1 || cols < 1) return Q4K_ERR_SHAPE;
+  size_t e;
+  if (!mul_ok(static_cast<size_t>(rows), static_cast<size_t>(cols), &e)) return Q4K_ERR_OVERFLOW;
+  if ((e + 255) / 256 > 0x7FFFFFFFu) return Q4K_ERR_OVERFLOW;  // grid of one value per thread
+  if (!aligned(x, 4) || !aligned(absmax, 4)) return Q4K_ERR_ALIGN;
+  const int st = check_device();
+  if (st) return st;
+  return launch_status(launch_fp8_quantize_rows(x, rows, cols, absmax, q, static_cast<hipStream_t>(stream)));
+}
+
+int fp8_gemm_dequant(const uint8_t* a, const float* a_absmax, const uint8_t* w, const float* w_absmax, float* y,
+                     int m, int n, int k, void* stream) {
+  if (!a || !a_absmax || !w || !w_absmax || !y) return Q4K_ERR_NULL;
+  if (m < 1 || m > kPrefillMaxM || n < 1 || k < 16 || k % 16 != 0 || k > kPrefillMaxK) return Q4K_ERR_SHAPE;
+  if ((static_cast<size_t>(n) + 127) / 128 > 0x7FFFFFFFu) return Q4K_ERR_SHAPE;
+  size_t e;
+  if (!mul_ok(static_cast<size_t>(m), static_cast<size_t>(n), &e) ||
+      !mul_ok(static_cast<size_t>(m), static_cast<size_t>(k), &e) ||
+      !mul_ok(static_cast<size_t>(n), static_cast<size_t>(k), &e))
+    return Q4K_ERR_OVERFLOW;
+  if (!aligned(a, kAlign) || !aligned(w, kAlign) || !aligned(a_absmax, 4) || !aligned(w_absmax, 4) ||
+      !aligned(y, 4))
+    return Q4K_ERR_ALIGN;
+  const int st = check_device();
+  if (st) return st;
+  return launch_status(launch_fp8_gemm(a, a_absmax, w, w_absmax, y, m, n, k, static_cast<hipStream_t>(stream)));
+}
+
 size_t ffn_swiglu_q4k_workspace_bytes(int m, int hidden, int inter, int top_k, int regime) {
   FfnLayout L;
   if (!ffn_layout(m, hidden, inter, top_k, regime, &L)) return 0;

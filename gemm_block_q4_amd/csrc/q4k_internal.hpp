@@ -114,5 +114,14 @@ hipError_t launch_moe_combine(const float* y_pair, const float* wts, const int32
                               int top_k, int n_experts, int hidden, float* y, hipStream_t stream);
 
 
+// Per-row FP8 (E4M3) recipe.  absmax [rows] = max |x| of each f32 row;
+// q [rows][cols] = E4M3 codes of x * 448/absmax (16-byte paths when the
+// shapes and pointers allow, else one value per thread); y [m][n] =
+// bf16(A_fp8 . W_fp8^T) * (a/448) * (w/448) for k % 16 == 0 and k <= 2^20.
+hipError_t launch_fp8_absmax_rows(const float* x, int rows, int cols, float* absmax, hipStream_t stream);
+hipError_t launch_fp8_quantize_rows(const float* x, int rows, int cols, const float* absmax, uint8_t* q,
+                                    hipStream_t stream);
+hipError_t launch_fp8_gemm(const uint8_t* a, const float* a_absmax, const uint8_t* w, const float* w_absmax,
+                           float* y, int m, int n, int k, hipStream_t stream);
 
 }  // namespace q4k

@@ -114,6 +114,7 @@ DECODE_FFN_7B = 2     # hidden 4096, inter 11008, 1/4/8 tokens, outliers
 PREFILL_FFN = 3       # hidden 5120, inter 17408, 512/2048 tokens, bf16, outliers
 MOE_DECODE = 4        # 64 experts, top-8, 4 tokens, hidden 2048, inter 768
 LM_HEAD = 5           # Q6_K LM head GEMV: vocab 32000 x hidden 4096, 1 token
+FP8_PREFILL = 6       # per-row FP8 recipe on the prefill FFN shapes (f32 weights)
 
 GEMV_SWEEP_SHAPES = ((4096, 4096), (11008, 4096), (4096, 11008))
 
@@ -146,3 +147,11 @@ def lm_head_case(vocab: int = 32000, hidden: int = 4096, sub: int = 0, seed: int
     w = random_q6k(rng(LM_HEAD, TENSOR_GATE, sub, seed), vocab, hidden)
     x = activations(LM_HEAD, 1, hidden, outliers=False, sub=sub, seed=seed)
     return w, x
+
+
+def fp8_case(m: int, n: int, k: int, sub: int = 0, seed: int = 0):
+    """Per-row FP8 GEMM inputs: activations f32 [m, k] N(0, 1) with 0.1%
+    outliers x100 (as the prefill FFN's) and an f32 weight [n, k] N(0, 0.02)."""
+    x = activations(FP8_PREFILL, m, k, outliers=True, sub=sub, seed=seed)
+    w = (rng(FP8_PREFILL, TENSOR_GATE, sub, seed).standard_normal((n, k)) * 0.02).astype(np.float32)
+    return x, w

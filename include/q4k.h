@@ -220,6 +220,56 @@ int q4k_test_mmq_partials(const void* w, const int8_t* qs, int m, int n, int k,
    Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */
 int q4k_test_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
+/* Per-row FP8 (E4M3) prefill recipe ("aprender-serve 0.70.2 --
+   src/cuda/executor/layers/cublas_prefill/fp8_recipe.rs", module header,
+   fp8_absmax_rows, fp8_quantize_rows, fp8_dequant_outer).  Each activation
+   row (token) and each weight row (output channel) has its own scale
+   448/absmax; E4M3 is the OCP E4M3FN format (sign, 4 exponent bits with bias
+   7, 3 mantissa bits, largest finite value 448, code 0x7F/0xFF NaN, no
+   infinity).  A weight is quantised once with fp8_absmax_rows +
+   fp8_quantize_rows; per call the activations get the same two steps, then
+   fp8_gemm_dequant.
+
+   fp8_absmax_rows: absmax[r] = max_i |x[r][i]| (f32; x finite).
+   x: device f32 [rows][cols] row-major; absmax: device f32 [rows],
+   overwritten.  rows >= 1, cols >= 1; 4-byte alignment (rows of a multiple of
+   4 values at a 16-byte aligned x are read 16 bytes at a time).
+   Errors: Q4K_ERR_NULL, Q4K_ERR_SHAPE, Q4K_ERR_ALIGN, Q4K_ERR_OVERFLOW,
+   Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */
+int fp8_absmax_rows(const float* x, int rows, int cols, float* absmax, void* stream);
+
+/* fp8_quantize_rows: q[r][i] = E4M3 code of x[r][i] * s_r, with
+   s_r = 448 / absmax[r] as a correctly rounded binary32 quotient (absmax 0
+   taken as 1, so s_r = 448) and the binary32 product encoded to the nearest
+   E4M3 value, ties to even, magnitudes saturated at 448 (code 0x7E / 0xFE),
+   subnormals (multiples of 2^-9 below 2^-6) kept, zeros keeping their sign.
+   x: device f32 [rows][cols] row-major, finite (NaN input is not defined);
+   absmax: device f32 [rows] (normally fp8_absmax_rows of the same x);
+   q: device uint8 [rows][cols], overwritten.  rows >= 1, cols >= 1;
+   x and absmax 4-byte aligned (16-byte aligned x and q with cols % 16 == 0
+   take the vector path; results do not depend on the path).
+   Errors: Q4K_ERR_NULL, Q4K_ERR_SHAPE, Q4K_ERR_ALIGN, Q4K_ERR_OVERFLOW,
+   Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */
+int fp8_quantize_rows(const float* x, int rows, int cols, const float* absmax, uint8_t* q, void* stream);
+
+/* fp8_gemm_dequant: the FP8 GEMM and the outer dequant in one pass,
+     D[t][c] = sum_i A[t][i] * W[c][i]   (E4M3 values, f32 accumulation),
+     y[t][c] = (bf16(D[t][c]) * (a_absmax[t] / 448)) * (w_absmax[c] / 448),
+   where bf16() rounds to bfloat16 (nearest even) as the GEMM's BF16 output
+   does, each factor is a correctly rounded binary32 quotient with absmax 0
+   taken as 1, and the two products are binary32 in this order.  The products
+   of two E4M3 values are exact; only the f32 accumulation order differs from
+   an exact sum, by far less than one bfloat16 step of D.
+   a: device uint8 [m][k] E4M3 codes (tokens); a_absmax: device f32 [m];
+   w: device uint8 [n][k] E4M3 codes (weight rows); w_absmax: device f32 [n];
+   y: device f32 [m][n] row-major, overwritten.  1 <= m <= 4194240, n >= 1,
+   16 <= k <= 1048576, k % 16 == 0; a and w 16-byte aligned, the rest 4-byte
+   aligned.  NaN codes (0x7F, 0xFF) give NaN outputs.
+   Errors: Q4K_ERR_NULL, Q4K_ERR_SHAPE, Q4K_ERR_ALIGN, Q4K_ERR_OVERFLOW,
+   Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */
+int fp8_gemm_dequant(const uint8_t* a, const float* a_absmax, const uint8_t* w, const float* w_absmax, float* y,
+                     int m, int n, int k, void* stream);
+
 /* Host.  Workspace bytes ffn_swiglu_q4k needs for these sizes and regime
    (Q4K_REGIME_AUTO resolves by m as the call does); top_k = 0 for a dense
    FFN.  Returns 0 for invalid sizes. */

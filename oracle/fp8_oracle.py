@@ -134,24 +134,33 @@ def bf16_rne(v: np.ndarray) -> np.ndarray:
     return r.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
-def gemm_rows(a_codes: np.ndarray, a_absmax: np.ndarray, w_codes: np.ndarray,
-              w_absmax: np.ndarray) -> np.ndarray:
-    """Y [m, n] of the recipe: D = A_fp8 . W_fp8^T (exact sum), rounded to
-    BF16, widened, times ``a[t]/448`` then times ``w[c]/448`` in binary32
-    (``fp8_dequant_outer``; zero absmax taken as 1)."""
-    A = e4m3_decode(a_codes)
-    W = e4m3_decode(w_codes)
-    # every product of two E4M3 values is a multiple of 2^-18 below 2^18, so
-    # the sums stay exact in f64 while |D| < 2^35
-    D = A @ W.T
+def dequant_outer(D: np.ndarray, a_absmax: np.ndarray, w_absmax: np.ndarray) -> np.ndarray:
+    """``fp8_dequant_outer``: Y [m, n] from the GEMM result D [m, n] (f64
+    values, rounded here to binary32 and then BF16 as the GEMM's BF16 output
+    is), widened, times ``a[t]/448`` then times ``w[c]/448`` in binary32
+    (each factor a binary32 quotient, zero absmax taken as 1)."""
     Db = bf16_rne(D).astype(np.float32)
     am = np.asarray(a_absmax, dtype=np.float32)
     wm = np.asarray(w_absmax, dtype=np.float32)
     f1 = (np.where(am == 0, np.float32(1.0), am).astype(np.float32) / np.float32(E4M3_MAX)).astype(np.float32)
     f2 = (np.where(wm == 0, np.float32(1.0), wm).astype(np.float32) / np.float32(E4M3_MAX)).astype(np.float32)
     y = (Db * f1[:, None]).astype(np.float32)
-    y = (y * f2[None, :]).astype(np.float32)
-    return y
+    return (y * f2[None, :]).astype(np.float32)
+
+
+def gemm_codes(a_codes: np.ndarray, w_codes: np.ndarray) -> np.ndarray:
+    """D = A_fp8 . W_fp8^T as the exact sum of the decoded products (f64).
+
+    Every product of two E4M3 values is a multiple of 2^-18 below 2^18, so the
+    sums stay exact in f64 while |D| < 2^35."""
+    return e4m3_decode(a_codes) @ e4m3_decode(w_codes).T
+
+
+def gemm_rows(a_codes: np.ndarray, a_absmax: np.ndarray, w_codes: np.ndarray,
+              w_absmax: np.ndarray) -> np.ndarray:
+    """Y [m, n] of the recipe: the exact D of the two code matrices, then
+    ``dequant_outer``."""
+    return dequant_outer(gemm_codes(a_codes, w_codes), a_absmax, w_absmax)
 
 
 def gemm_rows_exact(a_codes, a_absmax, w_codes, w_absmax) -> np.ndarray:

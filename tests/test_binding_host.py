@@ -97,3 +97,38 @@ def test_ffn_sizes():
     raises("must live on the GPU", q4k.ffn_swiglu_q4k, u8(e * gu), u8(e * gu), u8(e * dn),
            f32(m * hidden), q4k.Q4K_F32, m, hidden, inter, n_experts=e, ids=ids, wts=wts,
            top_k=top_k, **args)
+
+
+def test_fp8_sizes():
+    rows, cols = 3, 64
+    raises("x: holds", q4k.fp8_absmax_rows, f32(rows * cols - 1), rows, cols, f32(rows))
+    raises("absmax: holds", q4k.fp8_absmax_rows, f32(rows * cols), rows, cols, f32(rows - 1))
+    raises("q: holds", q4k.fp8_quantize_rows, f32(rows * cols), rows, cols, f32(rows), u8(rows * cols - 1))
+    raises("q: dtype", q4k.fp8_quantize_rows, f32(rows * cols), rows, cols, f32(rows), f32(rows * cols))
+    m, n, k = 4, 8, 128
+    raises("a: holds", q4k.fp8_gemm_dequant, u8(m * k - 1), f32(m), u8(n * k), f32(n), f32(m * n), m, n, k)
+    raises("w_absmax: holds", q4k.fp8_gemm_dequant, u8(m * k), f32(m), u8(n * k), f32(n - 1), f32(m * n),
+           m, n, k)
+    raises("y: holds", q4k.fp8_gemm_dequant, u8(m * k), f32(m), u8(n * k), f32(n), f32(m * n - 1), m, n, k)
+    raises("must live on the GPU", q4k.fp8_gemm_dequant, u8(m * k), f32(m), u8(n * k), f32(n), f32(m * n),
+           m, n, k)
+
+
+def test_library_loaded_first_shares_torch_hip_runtime():
+    """Loading the library before anything imports torch still leaves one HIP
+    runtime in the process (the library binds to torch's), so torch's streams
+    and allocations are the library's too."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = ("import sys; sys.path.insert(0, %r)\n"
+              "from gemm_block_q4_amd import _binding\n"
+              "_binding.load_library()\n"
+              "import torch\n"
+              "maps = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+              "print(len(maps))\n" % root)
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="")
+    out = subprocess.run([sys.executable, "-c", script], capture_output=True, text=True, env=env,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout

@@ -203,3 +203,31 @@ def test_read_hook_validation(lib):
     assert r(P, 24, P, None) == 2        # not a multiple of 16
     assert r(P + 8, 16, P, None) == 3
     assert r(P, 16, P + 2, None) == 3
+
+
+def test_fp8_validation(lib):
+    a = lib.fp8_absmax_rows
+    assert a(None, 4, 16, P, None) == 1
+    assert a(P, 4, 16, None, None) == 1
+    assert a(P, 0, 16, P, None) == 2
+    assert a(P, 4, 0, P, None) == 2
+    assert a(P + 2, 4, 16, P, None) == 3           # f32 rows need 4 bytes
+    assert a(P, 4, 16, P + 1, None) == 3
+    q = lib.fp8_quantize_rows
+    assert q(P, 4, 16, P, None, None) == 1
+    assert q(P, 4, -1, P, P, None) == 2
+    assert q(P, 4, 16, P + 2, P, None) == 3
+    assert q(P, 1 << 30, 1 << 30, P, P, None) == 4  # one value per thread: grid too large
+    g = lib.fp8_gemm_dequant
+    assert g(P, P, P, P, None, 4, 64, 128, None) == 1
+    assert g(None, P, P, P, P, 4, 64, 128, None) == 1
+    assert g(P, P, P, P, P, 0, 64, 128, None) == 2
+    assert g(P, P, P, P, P, 4, 0, 128, None) == 2
+    assert g(P, P, P, P, P, 4, 64, 120, None) == 2    # k not a multiple of 16
+    assert g(P, P, P, P, P, 4, 64, 0, None) == 2
+    assert g(P, P, P, P, P, 4, 64, (1 << 20) + 16, None) == 2
+    assert g(P, P, P, P, P, 64 * 65535 + 1, 64, 128, None) == 2
+    assert g(P + 4, P, P, P, P, 4, 64, 128, None) == 3  # codes need 16 bytes
+    assert g(P, P, P + 8, P, P, 4, 64, 128, None) == 3
+    assert g(P, P + 2, P, P, P, 4, 64, 128, None) == 3
+    assert g(P, P, P, P, P + 2, 4, 64, 128, None) == 3

@@ -23,7 +23,7 @@ CHILD = r"""
 import sys, threading, traceback
 sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
 from gemm_block_q4_amd import _binding
-lib = _binding.load_library({lib!r})
+lib = _binding.load_library({lib!r}, share_torch_runtime=False)
 import test_capi_host as T
 cases = [getattr(T, n) for n in sorted(dir(T)) if n.startswith("test_") and n != "test_exports_every_declared_function"]
 errors = []

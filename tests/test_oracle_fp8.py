@@ -136,6 +136,27 @@ def test_gemm_against_python_loops():
     assert np.all(err <= 0.1 * np.linalg.norm(a, axis=1)[:, None] * np.linalg.norm(w, axis=1)[None, :] + 1e-12)
 
 
+def test_dequant_outer_hand_values():
+    # "fp8_recipe.rs", fp8_dequant_outer: D rounded to BF16, times a/448, times w/448
+    D = np.array([[1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -3.0]])
+    y = fp8.dequant_outer(D, np.array([448.0], np.float32), np.array([448.0, 0.0, 896.0, 224.0], np.float32))
+    # 1 + 2^-8 is the tie between 1 and 1 + 2^-7: even mantissa (1); 1 + 3 2^-8
+    # the tie between 1 + 2^-7 and 1 + 2^-6: even mantissa (1 + 2^-6)
+    assert y[0, 0] == np.float32(1.0)
+    assert y[0, 1] == np.float32(1.0) / np.float32(448.0)       # zero absmax taken as 1
+    assert y[0, 2] == np.float32(1.015625) * np.float32(2.0)
+    assert y[0, 3] == np.float32(-1.5)
+    # both factors applied: a = 224 halves every output
+    y2 = fp8.dequant_outer(D, np.array([224.0], np.float32), np.array([448.0, 448.0, 448.0, 448.0], np.float32))
+    assert list(y2[0]) == [0.5, 0.5, np.float32(1.015625) / 2, -1.5]
+    # the binary32 product order: (D * f1) * f2 with f1 = 3/448, f2 = 5/448
+    d = np.float32(1.5)
+    f1 = np.float32(3.0) / np.float32(448.0)
+    f2 = np.float32(5.0) / np.float32(448.0)
+    y3 = fp8.dequant_outer(np.array([[1.5]]), np.array([3.0], np.float32), np.array([5.0], np.float32))
+    assert y3[0, 0] == np.float32(np.float32(d * f1) * f2)
+
+
 def test_rejects_non_finite():
     with pytest.raises(ValueError):
         fp8.e4m3_encode(np.array([np.inf], np.float32))
