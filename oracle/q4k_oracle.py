@@ -465,6 +465,41 @@ def moe_decode(bank_gate, bank_up, bank_down, n_experts: int, hidden: int, inter
     return y
 
 
+def moe_prefill(bank_gate, bank_up, bank_down, n_experts: int, hidden: int, inter: int,
+                x: np.ndarray, ids: np.ndarray, wts: np.ndarray, tokens=None) -> np.ndarray:
+    """Top-k MoE FFN for many tokens at the prefill quantisation points.
+
+    "micro_moe.rs", ``DirectNvFp4MoeBf16::new`` / ``execute``: one group per
+    (token, selected expert) pair, each pair's FFN run on its expert's
+    matrices, combined per token with the routing weights.  Each pair's FFN
+    is the prefill FFN of ``ffn_prefill`` ("q4k_mmq.rs" pipeline: Q8_1(x),
+    MMQ gate and up, SwiGLU, h to f32 and Q8_1, MMQ down); every step is per
+    token, so a pair's result depends only on x[t] and its expert.
+    y[t] = sum over slots s, in slot order, of wts[t, s] * FFN_{ids[t, s]}(x[t]);
+    ``tokens`` selects the returned rows.  Returns f64 [len, hidden].
+    """
+    gu_bytes = q4k_weight_bytes(inter, hidden)
+    dn_bytes = q4k_weight_bytes(hidden, inter)
+    bank_gate = np.asarray(bank_gate, dtype=np.uint8).reshape(-1)
+    bank_up = np.asarray(bank_up, dtype=np.uint8).reshape(-1)
+    bank_down = np.asarray(bank_down, dtype=np.uint8).reshape(-1)
+    x = np.asarray(x, dtype=np.float32)
+    m, top_k = ids.shape
+    if tokens is None:
+        tokens = list(range(m))
+    y = np.zeros((len(tokens), hidden), dtype=np.float64)
+    for i, t in enumerate(tokens):
+        for s in range(top_k):
+            e = int(ids[t, s])
+            if not 0 <= e < n_experts:
+                raise ValueError("expert id out of range")
+            wg = bank_gate[e * gu_bytes:(e + 1) * gu_bytes]
+            wu = bank_up[e * gu_bytes:(e + 1) * gu_bytes]
+            wd = bank_down[e * dn_bytes:(e + 1) * dn_bytes]
+            y[i] += float(wts[t, s]) * ffn_prefill(wg, wu, wd, hidden, inter, x[t:t + 1])[0]
+    return y
+
+
 # -- acceptance metrics (used by the parity tests) -----------------------------
 
 def row_norms(w: np.ndarray, rows: int, cols: int) -> np.ndarray:

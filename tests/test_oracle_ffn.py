@@ -2,6 +2,7 @@
 import math
 
 import numpy as np
+import pytest
 
 import bruteforce as bf
 from oracle import q4k_oracle as orc
@@ -111,3 +112,57 @@ def test_moe_is_linear_in_routing_weights():
     assert np.abs(y - parts).max() <= 1e-12 * np.abs(y).max()
     assert np.allclose(wts.sum(1), 1.0, atol=1e-6)
     assert all(len(set(r)) == k for r in ids.tolist())
+
+
+def _dequant_pair_ffn(wg, wu, wd, hidden, inter, xt):
+    """One pair's prefill FFN from the dequantised matrices and the dequantised
+    Q8_1 vectors (plain f64 products, no integer MMQ path)."""
+    qx, dx, _ = orc.q8_1_quantize(xt)
+    xh = orc.q8_1_dequantize(qx, dx)
+    g = xh @ orc.dequantize(wg, inter, hidden).T
+    u = xh @ orc.dequantize(wu, inter, hidden).T
+    h = (g / (1.0 + np.exp(-g)) * u).astype(np.float32)
+    qh, dh, _ = orc.q8_1_quantize(h)
+    return orc.q8_1_dequantize(qh, dh) @ orc.dequantize(wd, hidden, inter).T
+
+
+def test_moe_prefill_against_dequantised_loops():
+    # "micro_moe.rs": one group per (token, selected expert); duplicate experts
+    # across tokens, and slots whose expert differs from the slot index
+    n_exp, hidden, inter, m, k = 5, 256, 512, 4, 3
+    bg, bu, bd = synth.moe_banks(46, n_exp, hidden, inter)
+    x = synth.activations(46, m, hidden, outliers=True)
+    ids = np.array([[4, 1, 2], [1, 3, 0], [2, 4, 1], [0, 1, 4]], dtype=np.int32)
+    wts = np.array([[0.5, 0.25, 0.25], [0.7, 0.2, 0.1], [0.1, 0.1, 0.8], [0.3, 0.3, 0.4]], np.float32)
+    y = orc.moe_prefill(bg, bu, bd, n_exp, hidden, inter, x, ids, wts)
+    gb = orc.q4k_weight_bytes(inter, hidden)
+    db = orc.q4k_weight_bytes(hidden, inter)
+    for t in range(m):
+        ref = np.zeros(hidden)
+        for s in range(k):
+            e = ids[t, s]
+            ref += float(wts[t, s]) * _dequant_pair_ffn(bg[e * gb:(e + 1) * gb], bu[e * gb:(e + 1) * gb],
+                                                         bd[e * db:(e + 1) * db], hidden, inter,
+                                                         x[t:t + 1])[0]
+        assert np.abs(y[t] - ref).max() <= 1e-9 * np.abs(ref).max()
+    # a token subset returns the same rows
+    sub = orc.moe_prefill(bg, bu, bd, n_exp, hidden, inter, x, ids, wts, tokens=[3, 1])
+    assert np.array_equal(sub, y[[3, 1]])
+
+
+def test_moe_prefill_top1_is_the_dense_prefill_expert():
+    n_exp, hidden, inter, m = 3, 256, 256, 3
+    bg, bu, bd = synth.moe_banks(47, n_exp, hidden, inter)
+    x = synth.activations(47, m, hidden, outliers=False)
+    ids = np.array([[2], [2], [0]], dtype=np.int32)
+    wts = np.ones((m, 1), dtype=np.float32)
+    y = orc.moe_prefill(bg, bu, bd, n_exp, hidden, inter, x, ids, wts)
+    gb = orc.q4k_weight_bytes(inter, hidden)
+    db = orc.q4k_weight_bytes(hidden, inter)
+    for t in range(m):
+        e = ids[t, 0]
+        ref = orc.ffn_prefill(bg[e * gb:(e + 1) * gb], bu[e * gb:(e + 1) * gb], bd[e * db:(e + 1) * db],
+                              hidden, inter, x[t:t + 1])
+        assert np.array_equal(y[t], ref[0])
+    with pytest.raises(ValueError):
+        orc.moe_prefill(bg, bu, bd, n_exp, hidden, inter, x, np.array([[3], [0], [1]], np.int32), wts)
