@@ -376,6 +376,38 @@ def moe_ffn(q4k, synth, reps=40):
                 weight_gbs=round(distinct * per_expert / (us * 1e-6) / 1e9, 1))
 
 
+def moe_prefill(q4k, synth, reps=6):
+    """Top-k MoE FFN in the prefill regime (grouped MMQ passes): the routed
+    workload's 64 experts, top-8, 2048/768, at 512 and 2048 tokens; TOPS over
+    the pairs' 2 * 3 * hidden * inter ops each, on rotated bank copies."""
+    import torch
+    n_exp, hidden, inter, k = 64, 2048, 768, 8
+    bg, bu, bd = synth.moe_banks(synth.MOE_DECODE, n_exp, hidden, inter)
+    bank = q4k.q4k_weight_bytes(inter, hidden) * n_exp
+    copies = rotated(np.concatenate([bg, bu, bd]), max_copies=6)
+    out = {}
+    for m in (512, 2048):
+        x = torch.from_numpy(synth.activations(synth.MOE_DECODE, m, hidden, True, sub=m)).cuda()
+        ids_np, wts_np = synth.router(synth.MOE_DECODE, m, n_exp, k, seed=m)
+        ids = torch.from_numpy(ids_np).cuda()
+        wts = torch.from_numpy(wts_np).cuda()
+        y = torch.empty((m, hidden), dtype=torch.float32, device="cuda")
+        ws = torch.empty(q4k.ffn_swiglu_q4k_workspace_bytes(m, hidden, inter, k), dtype=torch.uint8,
+                         device="cuda")
+
+        def call(i):
+            c = copies[i % len(copies)]
+            q4k.ffn_swiglu_q4k(c[:bank], c[bank:2 * bank], c[2 * bank:], x, q4k.Q4K_F32, m, hidden,
+                               inter, y, ws, n_experts=n_exp, ids=ids, wts=wts, top_k=k)
+
+        us, _, _ = median_us(call, reps)
+        ops = 2.0 * m * k * 3 * hidden * inter
+        out[f"m{m}"] = dict(us_per_ffn=round(us, 1), tops=round(ops / (us * 1e-6) / 1e12, 1),
+                            frac_int8_peak=round(ops / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4),
+                            tokens_per_s=round(m / (us * 1e-6), 1))
+    return out
+
+
 def fp8_recipe(q4k, synth, reps=6):
     """Per-row FP8 recipe on the prefill FFN's projection shapes (gate/up
     [17408, 5120] and down [5120, 17408]) at 512 and 2048 tokens: the
@@ -546,6 +578,8 @@ def main():
         secondary["mmq_store_5120_17408_m2048"] = mmq_store(q4k, synth)
         log("bench: Q6_K LM head GEMV")
         secondary["lm_head_q6k_32000_4096"] = lm_head_q6k(q4k, synth)
+        log("bench: MoE prefill (grouped MMQ)")
+        secondary["moe_prefill_64x_top8_2048_768"] = moe_prefill(q4k, synth)
         log("bench: per-row FP8 recipe")
         secondary["fp8_recipe_5120_17408"] = fp8_recipe(q4k, synth)
 

@@ -126,7 +126,14 @@ struct FfnLayout {
   // prefill pass leaves it unwritten, and the span qx .. qh holds the
   // prefill down pass's k-split partial sums)
   size_t qx = 0, dx = 0, qh = 0, dh = 0;
+  // MoE prefill: the pairs sorted by expert, the tile table and its count
+  // (qh, dh: Q8_1(h) of the pairs in sorted order; y_pair: pair outputs)
+  size_t list = 0, tiles = 0, count = 0;
+  int max_tiles = 0;
 };
+
+// Token rows per tile of the grouped MoE prefill passes (the MMQ tile).
+constexpr int kMoeTileRows = 128;
 
 int resolve_regime(int regime, int m) {
   if (regime == Q4K_REGIME_AUTO) return m <= Q4K_DECODE_MAX_TOKENS ? Q4K_REGIME_DECODE : Q4K_REGIME_PREFILL;
@@ -141,7 +148,7 @@ bool ffn_layout(int m, int hidden, int inter, int top_k, int regime, FfnLayout* 
     return false;
   if ((regime == Q4K_REGIME_DECODE || regime == Q4K_REGIME_DECODE_Q8) && m > Q4K_DECODE_MAX_TOKENS)
     return false;
-  if (top_k > 0 && regime != Q4K_REGIME_DECODE) return false;
+  if (top_k > 0 && regime == Q4K_REGIME_DECODE_Q8) return false;
   const size_t M = static_cast<size_t>(m), H = static_cast<size_t>(hidden), I = static_cast<size_t>(inter);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -149,7 +156,20 @@ bool ffn_layout(int m, int hidden, int inter, int top_k, int regime, FfnLayout* 
     off = round_up(off + bytes, kWsAlign);
     return at;
   };
-  if (top_k > 0) {
+  if (top_k > 0 && regime == Q4K_REGIME_PREFILL) {
+    const size_t pairs = M * static_cast<size_t>(top_k);
+    if (pairs > static_cast<size_t>(INT32_MAX) || pairs * H > (SIZE_MAX / 8) || pairs * I > (SIZE_MAX / 8))
+      return false;
+    L->max_tiles = moe_route_max_tiles(static_cast<int>(pairs), kMoeRouteMaxExperts, kMoeTileRows);
+    L->qx = take(M * H);
+    L->dx = take(M * H / 32 * 4);
+    L->list = take(pairs * 4);
+    L->tiles = take(static_cast<size_t>(L->max_tiles) * 16);
+    L->count = take(4);
+    L->qh = take(pairs * I);
+    L->dh = take(pairs * I / 32 * 4);
+    L->y_pair = take(pairs * H * 4);
+  } else if (top_k > 0) {
     const size_t pairs = M * static_cast<size_t>(top_k);
     L->h = take(pairs * I * 4);
     L->y_pair = take(pairs * H * 4);
@@ -429,7 +449,19 @@ int ffn_common(const void* w_gate, const void* w_up, const void* w_down, int n_e
   const int reg = resolve_regime(regime, m);
   const bool decode = reg == Q4K_REGIME_DECODE || reg == Q4K_REGIME_DECODE_Q8;
   if (decode && m > Q4K_DECODE_MAX_TOKENS) return Q4K_ERR_SHAPE;
-  if (moe && reg != Q4K_REGIME_DECODE) return Q4K_ERR_SHAPE;
+  if (moe && reg == Q4K_REGIME_DECODE_Q8) return Q4K_ERR_SHAPE;
+  if (moe && reg == Q4K_REGIME_PREFILL) {
+    // the routing kernel's per-expert counters live in LDS; the gate/up pass
+    // addresses Q8_1(x) by token row with 32-bit offsets
+    if (n_experts > kMoeRouteMaxExperts) return Q4K_ERR_SHAPE;
+    if (static_cast<long long>(m) * top_k <= INT32_MAX &&
+        moe_route_max_tiles(m * top_k, n_experts, kMoeTileRows) > 65535)  // grid rows of the passes
+      return Q4K_ERR_SHAPE;
+    if (static_cast<long long>(m) * hidden > (1ll << 31) ||
+        static_cast<long long>(m) * top_k * inter > (1ll << 31) ||
+        static_cast<long long>(m) * top_k > INT32_MAX)
+      return Q4K_ERR_OVERFLOW;
+  }
   if (decode && (hidden > kDecodeMaxK || inter > kDecodeMaxK)) return Q4K_ERR_SHAPE;
   if (reg == Q4K_REGIME_PREFILL && (m > kPrefillMaxM || hidden > kPrefillMaxK || inter > kPrefillMaxK))
     return Q4K_ERR_SHAPE;
@@ -464,6 +496,63 @@ int ffn_common(const void* w_gate, const void* w_up, const void* w_down, int n_e
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* h = reinterpret_cast<float*>(ws + L.h);
+
+  if (moe && reg == Q4K_REGIME_PREFILL) {
+    // Grouped prefill ("micro_moe.rs": one group per (token, selection)
+    // pair; "q4k_mmq.rs" prefill pipeline per group): x -> Q8_1 per token;
+    // the pairs sorted by expert and cut into 128-row tiles; one grouped
+    // gate/up MMQ over every (expert, row tile) that gathers its pairs'
+    // token rows and writes Q8_1(silu(g)*u) in sorted order; one grouped
+    // down MMQ over those rows that writes each pair's output row; the
+    // slot-order weighted combine.
+    const int pairs = m * top_k;
+    int8_t* qx = reinterpret_cast<int8_t*>(ws + L.qx);
+    uint32_t* dx = reinterpret_cast<uint32_t*>(ws + L.dx);
+    int32_t* list = reinterpret_cast<int32_t*>(ws + L.list);
+    int32_t* tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+    int32_t* count = reinterpret_cast<int32_t*>(ws + L.count);
+    int8_t* qh = reinterpret_cast<int8_t*>(ws + L.qh);
+    uint32_t* dh = reinterpret_cast<uint32_t*>(ws + L.dh);
+    float* y_pair = reinterpret_cast<float*>(ws + L.y_pair);
+    const int grid_rows = moe_route_max_tiles(pairs, n_experts, kMoeTileRows);
+    hipError_t e = launch_q8_1_quantize(x, x_dtype == Q4K_BF16, m, hidden, qx, dx, s);
+    if (e != hipSuccess) return Q4K_ERR_LAUNCH;
+    if ((e = launch_moe_route(ids, pairs, n_experts, kMoeTileRows, list, tiles, count, s)) != hipSuccess)
+      return Q4K_ERR_LAUNCH;
+    MmqArgs gu{};
+    gu.w = static_cast<const uint8_t*>(w_gate);
+    gu.w_up = static_cast<const uint8_t*>(w_up);
+    gu.qs = qx;
+    gu.ds = dx;
+    gu.q_out = qh;
+    gu.d_out = dh;
+    gu.m = m;
+    gu.n = inter;
+    gu.k = hidden;
+    gu.group_tiles = tiles;
+    gu.group_count = count;
+    gu.group_list = list;
+    gu.group_mat_bytes = gu_bytes;
+    gu.group_top_k = top_k;
+    gu.group_grid_rows = grid_rows;
+    if ((e = launch_mmq(gu, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
+    MmqArgs dn{};
+    dn.w = static_cast<const uint8_t*>(w_down);
+    dn.qs = qh;
+    dn.ds = dh;
+    dn.y = y_pair;
+    dn.m = pairs;
+    dn.n = hidden;
+    dn.k = inter;
+    dn.group_tiles = tiles;
+    dn.group_count = count;
+    dn.group_list = list;
+    dn.group_mat_bytes = dn_bytes;
+    dn.group_scatter = 1;
+    dn.group_grid_rows = grid_rows;
+    if ((e = launch_mmq(dn, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
+    return launch_status(launch_moe_combine(y_pair, wts, ids, m, top_k, n_experts, hidden, y, s));
+  }
 
   if (moe) {
     // Gate/up: every (token, slot) pair is an independent pass over its

@@ -135,9 +135,11 @@ struct LoadOffsets {
   uint32_t wq, wh, xq[2], xd;
 };
 
-template <bool GU, bool PARTIALS>
+// GATHER (grouped gate/up pass): activation row t of the tile is qs/ds row
+// group_list[t0 + t] / group_top_k, relative to the whole qs/ds.
+template <bool GU, bool PARTIALS, bool GATHER>
 __device__ __forceinline__ LoadOffsets load_offsets(const MmqArgs& a, int K, int nsub, int rows,
-                                                    int toks, int tid) {
+                                                    int t0, int toks, int tid) {
   LoadOffsets o;
   {
     const int lr = tid >> 2, c = tid & 3;
@@ -148,15 +150,19 @@ __device__ __forceinline__ LoadOffsets load_offsets(const MmqArgs& a, int K, int
     const int r = Geometry<GU>::row(tid & 127);
     o.wh = r < rows ? static_cast<uint32_t>(r * K) * kBlockBytes : kOob;
   }
+  auto src_row = [&](int t) {
+    if constexpr (GATHER) return a.group_list[t0 + t] / a.group_top_k;
+    else return t;
+  };
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int idx = tid + i * kThreads;
     const int t = idx >> 3, c = idx & 7;
-    o.xq[i] = t < toks ? static_cast<uint32_t>(t) * a.k + 16u * c : kOob;
+    o.xq[i] = t < toks ? static_cast<uint32_t>(src_row(t)) * a.k + 16u * c : kOob;
   }
   {
     const int t = tid & 127, jj = tid >> 7;
-    o.xd = !PARTIALS && t < toks ? (static_cast<uint32_t>(t) * nsub + jj) * 4u : kOob;
+    o.xd = !PARTIALS && t < toks ? (static_cast<uint32_t>(src_row(t)) * nsub + jj) * 4u : kOob;
   }
   return o;
 }
@@ -253,7 +259,9 @@ __device__ __forceinline__ void store_stage(Stage& S, const Loads& L, int wave, 
   }
 }
 
-template <bool GU, bool PARTIALS>
+// GRP: grouped (MoE prefill) pass, the tile from a.group_tiles; GATHER: its
+// activation rows gathered through a.group_list (the gate/up pass).
+template <bool GU, bool PARTIALS, bool GRP, bool GATHER>
 __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   Stage* stages = reinterpret_cast<Stage*>(smem);
@@ -263,22 +271,37 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;  // wm 0..3: token tile; wn 0..1: weight half
-  const int t0 = blockIdx.y * kBM;
   const int n0 = blockIdx.x * RPM;
   const int K = a.k / kQK;
   const int nsub = a.k / kSub;
   const int rows = min(RPM, a.n - n0);
-  const int toks = min(kBM, a.m - t0);
+  int t0, toks;
+  size_t wofs = static_cast<size_t>(n0) * K * kBlockBytes;
+  if constexpr (GRP) {
+    // tile g: {expert, first row of the sorted row space, rows}; grid rows
+    // past the tile count exit before touching anything
+    const int g = blockIdx.y;
+    if (g >= *a.group_count) return;
+    const int4 td = reinterpret_cast<const int4*>(a.group_tiles)[g];
+    t0 = __builtin_amdgcn_readfirstlane(td.y);
+    toks = __builtin_amdgcn_readfirstlane(td.z);
+    wofs += static_cast<size_t>(__builtin_amdgcn_readfirstlane(td.x)) * a.group_mat_bytes;
+  } else {
+    t0 = blockIdx.y * kBM;
+    toks = min(kBM, a.m - t0);
+  }
 
   // resources: this workgroup's weight rows of each matrix and token rows
-  const size_t wofs = static_cast<size_t>(n0) * K * kBlockBytes;
+  // (a gathering pass addresses all of qs/ds by token row)
   const uint32_t wbytes = static_cast<uint32_t>(rows) * static_cast<uint32_t>(K) * kBlockBytes;
   const rsrc_t rw0 = make_rsrc(a.w + wofs, wbytes);
   const rsrc_t rw1 = GU ? make_rsrc(a.w_up + wofs, wbytes) : rw0;
-  const rsrc_t rx = make_rsrc(a.qs + static_cast<size_t>(t0) * a.k, static_cast<uint32_t>(toks) * a.k);
+  const size_t xrow0 = GATHER ? 0 : static_cast<size_t>(t0);
+  const uint32_t xrows = GATHER ? static_cast<uint32_t>(a.m) : static_cast<uint32_t>(toks);
+  const rsrc_t rx = make_rsrc(a.qs + xrow0 * a.k, xrows * a.k);
   // (no activation scales in the partials hook: an empty resource)
-  const rsrc_t rd = make_rsrc(a.ds ? a.ds + static_cast<size_t>(t0) * nsub : a.ds,
-                              a.ds && !PARTIALS ? static_cast<uint32_t>(toks) * nsub * 4u : 0u);
+  const rsrc_t rd = make_rsrc(a.ds ? a.ds + xrow0 * nsub : a.ds,
+                              a.ds && !PARTIALS ? xrows * nsub * 4u : 0u);
 
   // this lane's operand rows: weight tile wt in {0, 1} -> LDS weight row
   const int r32 = lane & 31;
@@ -305,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
   const int kb1 = min(K, kb0 + a.split_blocks);
   const int hb0 = 2 * kb0, hb1 = 2 * kb1;
 
-  const LoadOffsets lo = load_offsets<GU, PARTIALS>(a, K, nsub, rows, toks, tid);
+  const LoadOffsets lo = load_offsets<GU, PARTIALS, GATHER>(a, K, nsub, rows, t0, toks, tid);
   // Staging loads run two half blocks ahead of the compute: L0 holds even
   // half blocks, L1 odd ones, and the loop covers one whole block (two half
   // blocks) per iteration so that both register sets keep fixed names.
@@ -459,7 +482,8 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
   if constexpr (!PARTIALS) {
     // lane holds token xtok and, per tile, rows 8*(i/4) + 4*kh + i%4
     if (xtok < toks) {
-      const size_t roff = blockIdx.z * a.split_stride + static_cast<size_t>(t0 + xtok) * a.n;
+      const int orow = GRP && a.group_scatter ? a.group_list[t0 + xtok] : t0 + xtok;
+      const size_t roff = blockIdx.z * a.split_stride + static_cast<size_t>(orow) * a.n;
       if constexpr (GU) {
         if (a.q_out == nullptr) {
           float* yrow = a.y + roff;
@@ -493,12 +517,12 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
   }
 }
 
-template <bool GU, bool PARTIALS>
+template <bool GU, bool PARTIALS, bool GRP = false, bool GATHER = false>
 hipError_t launch(const MmqArgs& a, hipStream_t stream) {
   constexpr int RPM = Geometry<GU>::kRowsPerMatrix;
-  const dim3 grid((a.n + RPM - 1) / RPM, (a.m + kBM - 1) / kBM, a.splits);
+  const dim3 grid((a.n + RPM - 1) / RPM, GRP ? a.group_grid_rows : (a.m + kBM - 1) / kBM, a.splits);
   const size_t lds = 2 * sizeof(Stage);
-  auto kern = mmq_kernel<GU, PARTIALS>;
+  auto kern = mmq_kernel<GU, PARTIALS, GRP, GATHER>;
   const hipError_t e = lds_opt_in(reinterpret_cast<const void*>(kern), lds);
   if (e != hipSuccess) return e;
   kern<<<grid, dim3(kThreads), lds, stream>>>(a);
@@ -518,6 +542,18 @@ hipError_t launch_mmq(const MmqArgs& args, hipStream_t stream) {
     a.split_stride = 0;
   } else if (a.split_blocks < 1 || static_cast<long long>(a.splits - 1) * a.split_blocks >= K) {
     return hipErrorInvalidValue;  // every split must own at least one block
+  }
+  if (a.group_tiles) {
+    // grouped passes: the fused gate/up pass gathers token rows and writes
+    // Q8_1(h) in sorted order; the down pass reads those rows and scatters
+    if (!a.group_count || !a.group_list || a.partials || a.y_bf16 || a.group_grid_rows < 1)
+      return hipErrorInvalidValue;
+    if (a.w_up) {
+      if (!a.q_out || a.group_top_k < 1 || a.group_scatter) return hipErrorInvalidValue;
+      return launch<true, false, true, true>(a, stream);
+    }
+    if (a.group_top_k != 0) return hipErrorInvalidValue;
+    return launch<false, false, true, false>(a, stream);
   }
   if (a.partials) return a.w_up ? launch<true, true>(a, stream) : launch<false, true>(a, stream);
   return a.w_up ? launch<true, false>(a, stream) : launch<false, false>(a, stream);

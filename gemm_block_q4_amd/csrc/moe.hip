@@ -1,11 +1,13 @@
-// Small-batch top-k MoE: the combine step, gfx950.
+// Top-k MoE: routing for the grouped prefill pass and the combine step, gfx950.
 //
 // "libmir-cuda 0.1.0 -- .../nvfp4/selected/micro_moe.rs",
-// DirectNvFp4MoeBf16::execute: per token a list of selected expert ids and a
-// routing weight per selection.  The expert passes of the FFN write one
-// output row per (token, slot) pair; this kernel adds the top_k weighted
-// pair rows of every token in slot order (deterministic), skipping pairs
-// whose id is outside [0, n_experts).
+// DirectNvFp4MoeBf16::new / execute: per token a list of selected expert ids
+// and a routing weight per selection; one group per (token, selection) pair.
+// The routing kernel sorts the pairs by expert and cuts each expert's run
+// into row tiles for the grouped MMQ passes.  The expert passes of the FFN
+// write one output row per (token, slot) pair; the combine kernel adds the
+// top_k weighted pair rows of every token in slot order (deterministic),
+// skipping pairs whose id is outside [0, n_experts).
 #include "q4k_device.hpp"
 #include "q4k_internal.hpp"
 
@@ -41,6 +43,59 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   y[static_cast<size_t>(t) * hidden + c] = acc;
 }
 
+// One workgroup: per-expert pair counts by LDS atomics, an exclusive scan of
+// the counts and of the tile counts over the experts (wavefront 0: a run of
+// experts per lane, then a lane scan), the tile table, then every valid pair
+// placed at its expert's next list position.
+__global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restrict__ ids, int pairs,
+                                                         int n_experts, int tile_rows,
+                                                         int32_t* __restrict__ list,
+                                                         int4* __restrict__ tiles,
+                                                         int32_t* __restrict__ count) {
+  extern __shared__ int route_lds[];
+  int* cnt = route_lds;
+  int* cur = route_lds + n_experts;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < n_experts; e += 1024) cnt[e] = 0;
+  __syncthreads();
+  for (int p = tid; p < pairs; p += 1024) {
+    const int e = ids[p];
+    if (e >= 0 && e < n_experts) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const int per = (n_experts + 63) / 64;
+    const int lo = min(n_experts, tid * per), hi = min(n_experts, lo + per);
+    int rows = 0, ntiles = 0;
+    for (int e = lo; e < hi; ++e) {
+      rows += cnt[e];
+      ntiles += (cnt[e] + tile_rows - 1) / tile_rows;
+    }
+    int rs = rows, ts = ntiles;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int r = __shfl_up(rs, off, 64), t = __shfl_up(ts, off, 64);
+      if (tid >= off) {
+        rs += r;
+        ts += t;
+      }
+    }
+    int row = rs - rows, tile = ts - ntiles;
+    for (int e = lo; e < hi; ++e) {
+      const int c = cnt[e];
+      cur[e] = row;
+      for (int j = 0; j * tile_rows < c; ++j) tiles[tile++] = make_int4(e, row + j * tile_rows, min(tile_rows, c - j * tile_rows), 0);
+      row += c;
+    }
+    if (tid == 63) count[0] = ts;
+  }
+  __syncthreads();
+  for (int p = tid; p < pairs; p += 1024) {
+    const int e = ids[p];
+    if (e >= 0 && e < n_experts) list[atomicAdd(&cur[e], 1)] = p;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_moe_combine(const float* y_pair, const float* wts, const int32_t* ids, int m,
@@ -49,6 +104,15 @@ hipError_t launch_moe_combine(const float* y_pair, const float* wts, const int32
   const dim3 grid((hidden + 255) / 256, m);
   moe_combine_kernel<<<grid, dim3(256), 0, stream>>>(y_pair, wts, ids, m, top_k, n_experts,
                                                      hidden, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_route(const int32_t* ids, int pairs, int n_experts, int tile_rows, int32_t* list,
+                            int32_t* tiles, int32_t* count, hipStream_t stream) {
+  if (n_experts < 1 || n_experts > kMoeRouteMaxExperts || pairs < 1 || tile_rows < 1) return hipErrorInvalidValue;
+  const size_t lds = 2 * sizeof(int) * static_cast<size_t>(n_experts);
+  moe_route_kernel<<<dim3(1), dim3(1024), lds, stream>>>(ids, pairs, n_experts, tile_rows, list,
+                                                         reinterpret_cast<int4*>(tiles), count);
   return hipGetLastError();
 }
 

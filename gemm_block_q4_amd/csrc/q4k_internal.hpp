@@ -78,6 +78,21 @@ struct MmqArgs {
   // one pass over all of k into y.
   int splits, split_blocks;
   size_t split_stride;
+  // Grouped (MoE prefill) pass when group_tiles is set: grid row g below
+  // *group_count runs tile g = {expert e, first row r0, rows, 0} of a row
+  // space sorted by expert; e's matrices sit at e * group_mat_bytes of w and
+  // w_up.  Row r of the tile reads qs/ds row group_list[r] / group_top_k
+  // (group_top_k > 0: the pairs' token rows) or row r (group_top_k == 0);
+  // q_out/d_out rows are r, y rows are group_list[r] (group_scatter) or r.
+  // group_grid_rows grid rows are launched; the rest exit at once.  No k
+  // split, no partials.
+  const int32_t* group_tiles;
+  const int32_t* group_count;
+  const int32_t* group_list;
+  size_t group_mat_bytes;
+  int group_top_k;
+  int group_scatter;
+  int group_grid_rows;
 };
 
 hipError_t launch_mmq(const MmqArgs& a, hipStream_t stream);
@@ -107,6 +122,18 @@ hipError_t launch_mmq_split_reduce(const float* parts, int splits, size_t stride
 // Plain read of `bytes` (a multiple of 16, 16-byte aligned) from `buf`, one
 // 16-byte load per thread; `sink` is written only for a fixed bit pattern.
 hipError_t launch_read_ceiling(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+// MoE routing for the grouped prefill pass: list [pairs] = the pair indices
+// with a valid id, sorted by expert (order within an expert unspecified);
+// tiles [max_tiles][4] = {expert, first list position, rows (<= tile_rows),
+// 0} covering each expert's positions in order; count[0] = number of tiles.
+// n_experts <= kMoeRouteMaxExperts; max_tiles >= moe_route_max_tiles(...).
+constexpr int kMoeRouteMaxExperts = 4096;
+inline int moe_route_max_tiles(int pairs, int n_experts, int tile_rows) {
+  return pairs / tile_rows + (n_experts < pairs ? n_experts : pairs) + 1;
+}
+hipError_t launch_moe_route(const int32_t* ids, int pairs, int n_experts, int tile_rows, int32_t* list,
+                            int32_t* tiles, int32_t* count, hipStream_t stream);
 
 // y[t] = sum_{s < top_k} wts[t][s] * y_pair[t * top_k + s] in slot order
 // (pairs with an id outside [0, n_experts) skipped).

@@ -294,9 +294,15 @@ size_t ffn_swiglu_q4k_workspace_bytes(int m, int hidden, int inter, int top_k, i
    with fused silu*mul -> h -> Q8_1 -> MMQ down; decode_q8 ("ffn.rs",
    fused_ffn_swiglu_gpu_true_dp4a) = x -> Q8_1 -> integer-dot gate/up GEMV
    with fused silu*mul -> h (f32) -> Q8_1 -> integer-dot down GEMV, the
-   prefill arithmetic for 1 <= m <= 8 tokens.  MoE needs the decode regime
-   (m <= 8).  hidden, inter: multiples of 256 (at most 32768 in the decode
-   regimes, at most 2^20 in the prefill regime).
+   prefill arithmetic for 1 <= m <= 8 tokens (dense only).  MoE in the
+   decode regime runs one GEMV pass per (token, slot) pair; MoE in the
+   prefill regime ("micro_moe.rs", DirectNvFp4MoeBf16::new: one group per
+   pair) sorts the pairs by expert on the device and runs one grouped MMQ
+   gate/up pass (token rows gathered, Q8_1(h) written per pair) and one
+   grouped MMQ down pass over every (expert, 128-pair tile), then the
+   slot-order combine; there n_experts <= 4096, m * hidden <= 2^31 and
+   m * top_k * inter <= 2^31.  hidden, inter: multiples of 256 (at most 32768
+   in the decode regimes, at most 2^20 in the prefill regime).
    workspace: device, at least ffn_swiglu_q4k_workspace_bytes(...) bytes.
    Errors: Q4K_ERR_NULL, Q4K_ERR_SHAPE, Q4K_ERR_ALIGN, Q4K_ERR_OVERFLOW,
    Q4K_ERR_WORKSPACE, Q4K_ERR_DEVICE, Q4K_ERR_LAUNCH. */

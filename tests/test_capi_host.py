@@ -116,8 +116,15 @@ def test_ffn_validation(lib):
     assert f(P, P, P, 4, P, 0, 1, 256, 768, P, None, 2, 0, P, P, ws, None) == 1
     # MoE top_k larger than the expert count
     assert f(P, P, P, 4, P, 0, 1, 256, 768, P, P, 5, 0, P, P, ws, None) == 2
-    # MoE forced into the prefill regime
-    assert f(P, P, P, 4, P, 0, 1, 256, 768, P, P, 2, 2, P, P, ws, None) == 2
+    # MoE in the prefill regime (grouped MMQ): needs its own, larger workspace,
+    # at most 4096 experts (the routing counters) and 32-bit token-row offsets
+    pre_ws = lib.ffn_swiglu_q4k_workspace_bytes(16, 256, 768, 2, 2)
+    assert pre_ws > ws
+    assert f(P, P, P, 4, P, 0, 1, 256, 768, P, P, 2, 2, P, P, ws, None) == 5
+    assert f(P, P, P, 4, P, 0, 16, 256, 768, P, P, 2, 0, P, P, ws, None) == 5   # auto: 16 tokens
+    assert f(P, P, P, 4097, P, 0, 16, 256, 768, P, P, 2, 2, P, P, 1 << 40, None) == 2
+    assert f(P, P, P, 4, P, 0, 1 << 20, 4096, 768, P, P, 2, 2, P, P, 1 << 50, None) == 4
+    assert f(P, P, P, 4, P, 0, 1 << 16, 256, 16384, P, P, 4, 2, P, P, 1 << 50, None) == 4
     # decode regime forced with too many tokens
     assert f(P, P, P, 1, P, 0, 9, 256, 768, None, None, 0, 1, P, P, ws, None) == 2
     # Q8_1 decode regime: at most 8 tokens, dense only, k bound of the decode GEMVs
@@ -146,7 +153,10 @@ def test_workspace_sizes(lib):
     assert w(2, 8192, 512, 2, 0) >= 4 * (512 + 8192) * 4
     assert w(0, 256, 256, 0, 0) == 0
     assert w(9, 256, 256, 0, 1) == 0      # decode regime caps m at 8
-    assert w(4, 256, 256, 2, 2) == 0      # MoE is decode-only
+    # MoE prefill: Q8_1(x), the sorted pair list and tile table, Q8_1(h) and
+    # the f32 output of every pair
+    assert w(4, 256, 256, 2, 2) >= 4 * (256 + 32) + 8 * (4 + 256 + 32 + 256 * 4)
+    assert w(64, 2048, 768, 8, 0) >= 64 * (2048 + 256) + 512 * (4 + 768 + 96 + 2048 * 4)
     # Q8_1 decode: Q8_1 of x and of h, and h in f32
     assert w(8, 4096, 11008, 0, 3) >= 8 * (4096 + 4096 // 32 * 4 + 11008 * 4 + 11008 + 11008 // 32 * 4)
     assert w(9, 256, 256, 0, 3) == 0
