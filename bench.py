@@ -42,10 +42,14 @@ ROTATE_BYTES = 1 << 30         # per rotated tensor set
 # WRITE_SIZE (each scaled by what it reads for a copy of known size; summary and commands in
 # profiles/gemv_d4_decode_sweep_hbm_traffic.md) for the kernel sources with these SHA-256
 # digests.  Reported only while the sources still match.
-TRAFFIC_SWEEP_BYTES = 61279864
+TRAFFIC_SWEEP_BYTES = 61134209
 TRAFFIC_SOURCES = {
     "gemm_block_q4_amd/csrc/gemv_valu.hip":
-        "094eb220de80c4311a76906daa74afab5fc87a363c377b585b77aa182bab1b42",
+        "d20872c7b87d3ba7c4bd904f7f38224ccfab167ec3538af256cce3f078b45825",
+    "gemm_block_q4_amd/csrc/slice_dot.hpp":
+        "2537bd57a417fc0675d828787fd917af1b119de52e1be70ef9f0d7168421d428",
+    "gemm_block_q4_amd/csrc/lane_reduce.hpp":
+        "81cf704adbded368721e276da797c733493ebe02c36c41b124b78709d1f364e1",
     "gemm_block_q4_amd/csrc/q4k_device.hpp":
         "532c6e881bd56ddab7a0e075b479fbab8468380451639a48865dc41a8cb9352e",
 }
@@ -53,8 +57,8 @@ TRAFFIC_SOURCES = {
 
 # the kernel the roofline describes (one token, dense): layout 1 (a row is one
 # wavefront) for k = 4096, layout 2 (a row spans wavefronts) for k = 11008
-GEMV_KERNEL = ("gemv_d4_kernel<false, false, 0, 1|2, 1|2, 4> (q4k_gemv, m=1; layout 1 for k=4096, "
-               "2 for k=11008)")
+GEMV_KERNEL = ("gemv_d4_kernel<false, false, 0, 1, 1, 4> for k = 4096 and "
+               "gemv_d4_kernel<false, false, 0, 2, 2, 2> for k = 11008 (q4k_gemv, m = 1)")
 
 
 def log(*a):
