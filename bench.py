@@ -520,6 +520,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--skip-secondary", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--secondary", default="",
+                    help="comma-separated secondary workload keys to run (default: all)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -568,24 +570,23 @@ def main():
 
     secondary = {}
     if not args.skip_secondary:
-        log("bench: decode FFN")
-        secondary["decode_ffn_4096_11008"] = decode_ffn(q4k, synth)
-        log("bench: prefill FFN")
-        secondary["prefill_ffn_5120_17408"] = prefill_ffn(q4k, synth)
-        log("bench: MoE")
-        secondary["moe_64x_top8_2048_768"] = moe_ffn(q4k, synth)
-        log("bench: Q8_1-activation GEMV")
-        secondary["q8_gemv_sweep"] = q8_gemv(q4k, synth)
-        log("bench: Q4_K quantiser")
-        secondary["q4k_quantize_11008_4096"] = quantize_q4k(q4k, synth)
-        log("bench: MMQ f32 and bf16 stores")
-        secondary["mmq_store_5120_17408_m2048"] = mmq_store(q4k, synth)
-        log("bench: Q6_K LM head GEMV")
-        secondary["lm_head_q6k_32000_4096"] = lm_head_q6k(q4k, synth)
-        log("bench: MoE prefill (grouped MMQ)")
-        secondary["moe_prefill_64x_top8_2048_768"] = moe_prefill(q4k, synth)
-        log("bench: per-row FP8 recipe")
-        secondary["fp8_recipe_5120_17408"] = fp8_recipe(q4k, synth)
+        workloads = (
+            ("decode_ffn_4096_11008", "decode FFN", decode_ffn),
+            ("prefill_ffn_5120_17408", "prefill FFN", prefill_ffn),
+            ("moe_64x_top8_2048_768", "MoE", moe_ffn),
+            ("q8_gemv_sweep", "Q8_1-activation GEMV", q8_gemv),
+            ("q4k_quantize_11008_4096", "Q4_K quantiser", quantize_q4k),
+            ("mmq_store_5120_17408_m2048", "MMQ f32 and bf16 stores", mmq_store),
+            ("lm_head_q6k_32000_4096", "Q6_K LM head GEMV", lm_head_q6k),
+            ("moe_prefill_64x_top8_2048_768", "MoE prefill (grouped MMQ)", moe_prefill),
+            ("fp8_recipe_5120_17408", "per-row FP8 recipe", fp8_recipe),
+        )
+        only = [w for w in args.secondary.split(",") if w] if args.secondary else []
+        for key, what, fn in workloads:
+            if only and key not in only:
+                continue
+            log(f"bench: {what}")
+            secondary[key] = fn(q4k, synth)
 
     cpu = None
     if not args.skip_cpu:
