@@ -9,8 +9,8 @@
 // slices of 64 weights (one quarter g of a 256-block: quant bytes 32g..32g+31,
 // low nibbles = sub-block 2g, high nibbles = sub-block 2g+1).  Each lane owns
 // one slice position for the whole kernel; the wavefront walks its rows and at
-// every row each lane streams its slice (two 16-byte loads, plus one 4-byte
-// word of the block header that the block's lane quad shares) and adds
+// every row each lane streams its slice (two 16-byte loads) and its block's
+// 16-byte header (the four lanes of a block load the same line) and adds
 //   d*sc_{2g} * sum q x  +  d*sc_{2g+1} * sum q x  -  dmin*(m_{2g} X_{2g} + m_{2g+1} X_{2g+1})
 // where X are the f32 sums of the slice's two halves of x.  Consecutive lanes
 // own consecutive quarters, so a wavefront's loads cover 16 consecutive blocks
