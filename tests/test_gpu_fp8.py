@@ -158,6 +158,17 @@ def test_gemm_dequant_envelope(lib, m, n, k):
     say(f"  {equal:.5f} of the outputs equal the oracle's")
 
 
+def test_gemm_maximum_k(lib):
+    # k = 2^20, the largest the entry point takes: 8192 stages of 128
+    m, n, k = 3, 5, 1 << 20
+    say(f"fp8 gemm maximum k m={m} n={n} k={k}")
+    x, w = synth.fp8_case(m, n, k, sub=77)
+    qa, aa = fp8.quantize_rows(x)
+    qw, wa = fp8.quantize_rows(w)
+    y = gemm_gpu(lib, qa, aa, qw, wa)
+    check_envelope(y, qa, aa, qw, wa, min_equal=0.0)
+
+
 def test_gemm_zero_rows_and_saturated_codes(lib):
     # all-zero token and weight rows (absmax 0, taken as 1), and rows of 448s:
     # |D| up to 448^2 k stays far inside the f32 and BF16 exponent range

@@ -100,3 +100,16 @@ def test_moe_prefill_two_calls_reuse_the_workspace(lib):
                            ids=dev(ids), wts=dev(wts), top_k=k)
         ref = orc.moe_prefill(*banks, n_exp, hidden, inter, x, ids, wts)
         assert orc.relative_l2(host(y), ref) <= TOL
+
+
+def test_moe_prefill_many_experts(lib):
+    # 300 experts (several per lane of the routing scan), top-4, most of them
+    # idle; pairs of one token on distinct experts
+    n_exp, hidden, inter, m, k = 300, 256, 256, 24, 4
+    say("moe prefill 300 experts top-4")
+    banks = synth.moe_banks(95, n_exp, hidden, inter)
+    x = synth.activations(95, m, hidden, outliers=True)
+    ids, wts = synth.router(95, m, n_exp, k)
+    y = moe_prefill_gpu(lib, banks, x, ids, wts, n_exp, hidden, inter)
+    ref = orc.moe_prefill(*banks, n_exp, hidden, inter, x, ids, wts)
+    assert orc.relative_l2(y, ref) <= TOL

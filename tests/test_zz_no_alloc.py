@@ -87,6 +87,22 @@ def test_noalloc_moe_two_calls(lib):
         assert orc.relative_l2(y_na, orc.moe_decode(*banks, n_exp, hidden, inter, x, ids, wts)) <= TOL
 
 
+def test_noalloc_moe_prefill_two_calls(lib):
+    # MoE above 8 tokens: the grouped prefill passes, their pair list, tile
+    # table and tile count in the scratch; the second call routes other pairs
+    n_exp, hidden, inter, k = 64, 2048, 768, 8
+    banks = synth.moe_banks(synth.MOE_DECODE, n_exp, hidden, inter)
+    for call, m in enumerate((200, 33)):
+        say(f"noalloc moe prefill 64 x top-8 2048/768 m={m} (call {call + 1})")
+        x = synth.activations(synth.MOE_DECODE, m, hidden, outliers=True, sub=m + 1)
+        ids, wts = synth.router(synth.MOE_DECODE, m, n_exp, k, seed=m)
+        y_ws, y_na = both(lib, *banks, x, hidden, inter, n_exp=n_exp, ids=ids, wts=wts)
+        assert np.array_equal(y_ws, y_na)
+        toks = [0, m // 2, m - 1]
+        ref = orc.moe_prefill(*banks, n_exp, hidden, inter, x, ids, wts, tokens=toks)
+        assert orc.relative_l2(y_na[toks], ref) <= TOL
+
+
 def test_noalloc_refuses_oversized_layout(lib):
     # 4096 prefill tokens of 5120/17408 need more than the fixed scratch:
     # refused before any launch
