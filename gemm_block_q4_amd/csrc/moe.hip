@@ -58,9 +58,17 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restri
   const int tid = threadIdx.x;
   for (int e = tid; e < n_experts; e += 1024) cnt[e] = 0;
   __syncthreads();
-  for (int p = tid; p < pairs; p += 1024) {
-    const int e = ids[p];
-    if (e >= 0 && e < n_experts) atomicAdd(&cnt[e], 1);
+  // eight ids per thread in flight at a time (one load round per 8192 pairs)
+  for (int p0 = 0; p0 < pairs; p0 += 8 * 1024) {
+    int e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = p0 + tid + 1024 * i;
+      e[i] = p < pairs ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (e[i] >= 0 && e[i] < n_experts) atomicAdd(&cnt[e[i]], 1);
   }
   __syncthreads();
   if (tid < 64) {
@@ -90,9 +98,16 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restri
     if (tid == 63) count[0] = ts;
   }
   __syncthreads();
-  for (int p = tid; p < pairs; p += 1024) {
-    const int e = ids[p];
-    if (e >= 0 && e < n_experts) list[atomicAdd(&cur[e], 1)] = p;
+  for (int p0 = 0; p0 < pairs; p0 += 8 * 1024) {
+    int e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = p0 + tid + 1024 * i;
+      e[i] = p < pairs ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (e[i] >= 0 && e[i] < n_experts) list[atomicAdd(&cur[e[i]], 1)] = p0 + tid + 1024 * i;
   }
 }
 
