@@ -153,11 +153,12 @@ __global__ __launch_bounds__(128 * WM) void fp8_gemm_kernel(const uint8_t* __res
   const int rows = min(kFBN, n - n0);
   const rsrc_t ra = make_rsrc(a + static_cast<size_t>(t0) * k, static_cast<uint32_t>(toks) * static_cast<uint32_t>(k));
   const rsrc_t rw = make_rsrc(w + static_cast<size_t>(n0) * k, static_cast<uint32_t>(rows) * static_cast<uint32_t>(k));
-  // chunk c = tid + kThreads i: row c / 8, 16-byte column c % 8 (the column is
-  // the same for every i since kThreads is a multiple of 8)
-  const int scol = 16 * (tid & 7);
-  const int srow0 = tid >> 3;
-  constexpr int kRowStep = kThreads / 8;
+  // chunk c = tid + kThreads i: row c / kFCh, 16-byte column c % kFCh (the
+  // column is the same for every i since kThreads is a multiple of kFCh)
+  constexpr int kFCh = kFK / 16;  // 16-byte chunks per staged row
+  const int scol = 16 * (tid % kFCh);
+  const int srow0 = tid / kFCh;
+  constexpr int kRowStep = kThreads / kFCh;
   uint4 la[kAChunks], lw[kWChunks];
   auto load = [&](int s) {
     const int col = s * kFK + scol;
@@ -275,9 +276,10 @@ hipError_t launch_fp8_quantize_rows(const float* x, int rows, int cols, const fl
 
 hipError_t launch_fp8_gemm(const uint8_t* a, const float* a_absmax, const uint8_t* w, const float* w_absmax,
                            float* y, int m, int n, int k, hipStream_t stream) {
-  // 256-token tiles when they still give every compute unit a workgroup
-  const long tiles256 = static_cast<long>((m + 255) / 256) * ((n + kFBN - 1) / kFBN);
-  if (tiles256 >= 256) return launch_gemm_wm<4>(a, a_absmax, w, w_absmax, y, m, n, k, stream);
+  // 128 x 128 tiles (four wavefronts, 74 KiB of LDS: two workgroups per
+  // compute unit).  256 x 128 tiles with eight wavefronts were slower or equal
+  // on every prefill shape (107 / 273 / 108 / 284 us against 98 / 270 / 108 /
+  // 245 us for gate/up and down at 512 / 2048 tokens), as were 64-byte k stages.
   return launch_gemm_wm<2>(a, a_absmax, w, w_absmax, y, m, n, k, stream);
 }
 

@@ -145,8 +145,8 @@ def test_codes_on_the_e4m3_grid(lib, pad_to):
 @pytest.mark.parametrize("m,n,k", [(1, 1, 16), (5, 37, 48), (130, 200, 272), (300, 384, 1024),
                                    (64, 128, 5120), (257, 129, 4096 + 16), (513, 16384 + 40, 64)])
 def test_gemm_dequant_envelope(lib, m, n, k):
-    # the last shape has enough 256-token tiles to take the wide-tile kernel;
-    # its outputs are checked on every 7th weight row and the ragged last tile
+    # the last shape's outputs are checked on every 7th weight row and the
+    # ragged last tile
     say(f"fp8 gemm m={m} n={n} k={k}")
     x, w = synth.fp8_case(m, n, k, sub=m + n + k)
     qa, aa = fp8.quantize_rows(x)
