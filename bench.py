@@ -42,10 +42,10 @@ ROTATE_BYTES = 1 << 30         # per rotated tensor set
 # WRITE_SIZE (each scaled by what it reads for a copy of known size; summary and commands in
 # profiles/gemv_d4_decode_sweep_hbm_traffic.md) for the kernel sources with these SHA-256
 # digests.  Reported only while the sources still match.
-TRAFFIC_SWEEP_BYTES = 61134209
+TRAFFIC_SWEEP_BYTES = 61134272
 TRAFFIC_SOURCES = {
     "gemm_block_q4_amd/csrc/gemv_valu.hip":
-        "d20872c7b87d3ba7c4bd904f7f38224ccfab167ec3538af256cce3f078b45825",
+        "24b1babb3e81b245208873f972c416fa1e84ca3f2775a593efa4e31554483a3e",
     "gemm_block_q4_amd/csrc/slice_dot.hpp":
         "2537bd57a417fc0675d828787fd917af1b119de52e1be70ef9f0d7168421d428",
     "gemm_block_q4_amd/csrc/lane_reduce.hpp":
