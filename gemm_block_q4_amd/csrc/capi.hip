@@ -614,6 +614,17 @@ int ffn_common(const void* w_gate, const void* w_up, const void* w_down, int n_e
     gu.n = inter;
     gu.k = hidden;
     gu.m = m;
+    // 2..8 tokens: the down pass may split k in two halves that add into y,
+    // which the gate/up pass zeroes; not when y overlaps x (an in-place call:
+    // x must stay intact until the gate/up pass has read it)
+    const size_t x_bytes = static_cast<size_t>(m) * hidden * (x_dtype == Q4K_BF16 ? 2 : 4);
+    const size_t y_bytes = static_cast<size_t>(m) * hidden * 4;
+    const uintptr_t xa = reinterpret_cast<uintptr_t>(x), ya = reinterpret_cast<uintptr_t>(y);
+    const bool split = gemv_mfma_splits(m, hidden, inter) == 2 && (ya + y_bytes <= xa || xa + x_bytes <= ya);
+    if (split) {
+      gu.zero_out = y;
+      gu.zero_n = m * hidden;
+    }
     hipError_t e = launch_gemv(gu, s);
     if (e != hipSuccess) return Q4K_ERR_LAUNCH;
     GemvArgs dn{};
@@ -626,6 +637,7 @@ int ffn_common(const void* w_gate, const void* w_up, const void* w_down, int n_e
     dn.n = hidden;
     dn.k = inter;
     dn.m = m;
+    if (split) dn.splits = 2;
     return launch_status(launch_gemv(dn, s));
   }
 

@@ -32,11 +32,17 @@
 // index 8*(l/16)+i of step s is weight 64*(l/16) + 8*s + i; the activation
 // operand uses the same K mapping.  Each wavefront converts its own
 // activation range a chunk of blocks at a time into LDS in operand layout.
+// Split mode (the down pass of the FFN, at most 256 row tiles): every row
+// group runs as two workgroups over the two halves of the blocks, which add
+// their sums to a y the gate/up pass has zeroed (each workgroup converts the
+// activations of half of k instead of all of it); 0 + a + b rounds the same
+// in either order, so the result is deterministic.
 // Every global load is a raw buffer load (out-of-range lanes read zero); the
 // weights of the next tile (or of the next chunk's first tile) and the next
 // chunk's activations are in flight while the current ones are multiplied,
 // and reductions across lanes use DPP.  The W partial tiles are added in a
 // fixed order at the end (deterministic).
+#include <algorithm>
 #include <type_traits>
 
 #include "q4k_device.hpp"
@@ -321,7 +327,7 @@ __device__ __forceinline__ void lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-template <int MT, bool GU, bool BF16, int W, int RT>
+template <int MT, bool GU, bool BF16, int W, int RT, bool SPLIT>
 __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(GemvArgs a) {
   constexpr int CH = WaveLds<MT>::kCH;
   constexpr int R2 = WaveLds<MT>::kR2;
@@ -334,6 +340,13 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(GemvArgs a) {
   // compiler wait for it at the join)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = a.k / kQK;
+  // the output of a later split launch (the down pass of the FFN) starts at
+  // zero: every workgroup clears a share of it
+  if (a.zero_out != nullptr) {
+    const int per = (a.zero_n + gridDim.x - 1) / gridDim.x;
+    const int z1 = min(a.zero_n, (static_cast<int>(blockIdx.x) + 1) * per);
+    for (int i = static_cast<int>(blockIdx.x) * per + tid; i < z1; i += 64 * W) a.zero_out[i] = 0.f;
+  }
 
   const int mt = min(a.m, MT);  // live tokens (rows of x and y)
   int tl[MT];                   // lane of each token's maximum in token_max
@@ -354,8 +367,12 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(GemvArgs a) {
   // resource is left unbounded
   const rsrc_t rx = make_rsrc(a.x, 0x7FFFFFFFu);
 
-  const int kb0 = (wave * K) / W;
-  const int kb1 = ((wave + 1) * K) / W;
+  // this workgroup's blocks (all of k, or split blockIdx.y), then this
+  // wavefront's share of them
+  const int ks0 = SPLIT ? static_cast<int>(blockIdx.y) * K / a.splits : 0;
+  const int ksn = (SPLIT ? (static_cast<int>(blockIdx.y) + 1) * K / a.splits : K) - ks0;
+  const int kb0 = ks0 + (wave * ksn) / W;
+  const int kb1 = ks0 + ((wave + 1) * ksn) / W;
 
   // byte offset of block cb + bi of this lane's row in tile r (kOob past the
   // workgroup's rows or the chunk's nbb blocks)
@@ -464,15 +481,20 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(GemvArgs a) {
       float s = 0.f;
 #pragma unroll
       for (int w = 0; w < W; ++w) s += lds.red[0][w][t][rr] + lds.red[0][w][HR + t][rr];
-      float out = s;
-      if constexpr (GU) {
-        float su = 0.f;
+      if constexpr (SPLIT) {
+        __hip_atomic_fetch_add(a.y + static_cast<size_t>(t) * a.ldy + n0 + r * kRows + rr, s, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        float out = s;
+        if constexpr (GU) {
+          float su = 0.f;
 #pragma unroll
-        for (int w = 0; w < W; ++w)
-          su += lds.red[GU ? 1 : 0][w][t][rr] + lds.red[GU ? 1 : 0][w][HR + t][rr];
-        out = silu_mul(s, su);
+          for (int w = 0; w < W; ++w)
+            su += lds.red[GU ? 1 : 0][w][t][rr] + lds.red[GU ? 1 : 0][w][HR + t][rr];
+          out = silu_mul(s, su);
+        }
+        a.y[static_cast<size_t>(t) * a.ldy + n0 + r * kRows + rr] = out;
       }
-      a.y[static_cast<size_t>(t) * a.ldy + n0 + r * kRows + rr] = out;
     }
   }
 }
@@ -482,11 +504,11 @@ hipError_t dispatch_w(const GemvArgs& a, const dim3& grid, hipStream_t stream) {
   const bool gu = a.w_up != nullptr;
   const bool bf = a.x_bf16 != 0;
   if (gu) {
-    if (bf) gemv_mfma_kernel<MT, true, true, W, RT><<<grid, dim3(64 * W), 0, stream>>>(a);
-    else gemv_mfma_kernel<MT, true, false, W, RT><<<grid, dim3(64 * W), 0, stream>>>(a);
+    if (bf) gemv_mfma_kernel<MT, true, true, W, RT, false><<<grid, dim3(64 * W), 0, stream>>>(a);
+    else gemv_mfma_kernel<MT, true, false, W, RT, false><<<grid, dim3(64 * W), 0, stream>>>(a);
   } else {
-    if (bf) gemv_mfma_kernel<MT, false, true, W, RT><<<grid, dim3(64 * W), 0, stream>>>(a);
-    else gemv_mfma_kernel<MT, false, false, W, RT><<<grid, dim3(64 * W), 0, stream>>>(a);
+    if (bf) gemv_mfma_kernel<MT, false, true, W, RT, false><<<grid, dim3(64 * W), 0, stream>>>(a);
+    else gemv_mfma_kernel<MT, false, false, W, RT, false><<<grid, dim3(64 * W), 0, stream>>>(a);
   }
   return hipGetLastError();
 }
@@ -513,11 +535,46 @@ hipError_t dispatch_m(const GemvArgs& a, hipStream_t stream) {
   return dispatch_rt<MT, 3>(a, tiles, stream);
 }
 
+// Split k: tiles per workgroup with two workgroups per row group, about 256
+// workgroups in all.
+int split_rt(int tiles) { return tiles <= 128 ? 1 : 2; }
+
+template <int MT, int RT>
+hipError_t dispatch_split_rt(const GemvArgs& a, int tiles, hipStream_t stream) {
+  // at most 256 tiles: at most 256 workgroups, eight wavefronts each
+  const dim3 grid((tiles + RT - 1) / RT, 2);
+  gemv_mfma_kernel<MT, false, false, kWavesMax, RT, true><<<grid, dim3(64 * kWavesMax), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t dispatch_split(const GemvArgs& a, hipStream_t stream) {
+  const int tiles = (a.n + kRows - 1) / kRows;
+  if (split_rt(tiles) == 1) return dispatch_split_rt<MT, 1>(a, tiles, stream);
+  return dispatch_split_rt<MT, 2>(a, tiles, stream);
+}
+
 }  // namespace
+
+// Two splits when the rows give at most 256 tiles of 16 (without them every
+// workgroup converts the activations of all of k for only 16 rows) and k has
+// at least 16 blocks (8 per half: one per wavefront).
+int gemv_mfma_splits(int m, int n, int k) {
+  if (m < 2 || m > 8) return 1;
+  const int tiles = (n + kRows - 1) / kRows;
+  return tiles <= 256 && k / kQK >= 16 ? 2 : 1;
+}
 
 // Tokens are rounded up to 4 or 8 (the operand holds hi and lo halves of up
 // to eight tokens either way).
 hipError_t launch_gemv_mfma(const GemvArgs& a, hipStream_t stream) {
+  if (a.splits > 1) {
+    // one dense f32 matrix, y zeroed by the caller
+    if (a.splits != 2 || a.w_up != nullptr || a.x_bf16 || a.ids != nullptr || (a.n + kRows - 1) / kRows > 256)
+      return hipErrorInvalidValue;
+    if (a.m <= 4) return dispatch_split<4>(a, stream);
+    return dispatch_split<8>(a, stream);
+  }
   if (a.m <= 4) return dispatch_m<4>(a, stream);
   return dispatch_m<8>(a, stream);
 }

@@ -39,7 +39,20 @@ struct GemvArgs {
   int top_k;
   int n_experts;
   int pairs;
+  // Split k (matrix-core kernel, one dense f32 matrix, 2..8 tokens):
+  // splits == 2 runs every row group as two workgroups over the two halves of
+  // the blocks, each adding its sums to y with atomic adds; y must be zero on
+  // entry.  0 + a + b rounds the same in either order, so the result does not
+  // depend on which half lands first.  splits <= 1: no split.
+  int splits;
+  // f32 values this launch sets to zero (for a later split launch), or nullptr
+  float* zero_out;
+  int zero_n;
 };
+
+// Splits (1 or 2) the matrix-core kernel takes for m tokens on an [n][k]
+// matrix when the caller has zeroed y.
+int gemv_mfma_splits(int m, int n, int k);
 
 // Dispatches to the VALU kernel (few tokens) or the matrix-core kernel.
 hipError_t launch_gemv(const GemvArgs& a, hipStream_t stream);

@@ -286,7 +286,8 @@ size_t ffn_swiglu_q4k_workspace_bytes(int m, int hidden, int inter, int top_k, i
    w_down: device bank of n_experts matrices [hidden][inter]; expert e's matrix
    starts at e * q4k_weight_bytes(rows, cols) in its bank ("micro_moe.rs",
    validate: gate and up equal, down transposed).
-   x: device [m][hidden] of x_dtype; y: device f32 [m][hidden], overwritten.
+   x: device [m][hidden] of x_dtype; y: device f32 [m][hidden], overwritten
+   (y may be x itself: every regime reads x completely before y is written).
    ids: device int32 [m][top_k]; wts: device f32 [m][top_k].  An id outside
    [0, n_experts) contributes nothing (device data is not read back).
    Regime: decode = f32 activations through the dequant-fused GEMV (gate and

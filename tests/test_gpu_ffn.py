@@ -102,6 +102,37 @@ def test_decode_ffn_wide_inter(lib, m):
     assert orc.relative_l2(y, orc.ffn_decode(wg, wu, wd, hidden, inter, x)) <= TOL
 
 
+@pytest.mark.parametrize("m,hidden,inter", [(2, 1024, 4096), (5, 2560, 8192), (8, 2560, 8192), (8, 768, 4352)])
+def test_decode_ffn_split_down(lib, m, hidden, inter):
+    # 2..8 tokens with the down pass's k split in two halves that add into y
+    # (zeroed by the gate/up pass): one or two row tiles per workgroup, an odd
+    # block count (17 = 8 + 9).  y starts as NaN, and a second call with other
+    # activations must not accumulate onto the first call's result.
+    say(f"ffn decode split down {hidden}/{inter} m={m}")
+    wg, wu, wd = synth.dense_ffn_weights(96, hidden, inter)
+    ws = workspace(lib, m, hidden, inter)
+    gw, uw, dw = dev(wg), dev(wu), dev(wd)
+    y = empty((m, hidden), torch.float32)
+    y.fill_(float("nan"))
+    for sub in (m, m + 100):
+        x = synth.activations(96, m, hidden, outliers=True, sub=sub)
+        lib.ffn_swiglu_q4k(gw, uw, dw, dev(x), lib.Q4K_F32, m, hidden, inter, y, ws)
+        assert orc.relative_l2(host(y), orc.ffn_decode(wg, wu, wd, hidden, inter, x)) <= TOL
+
+
+def test_decode_ffn_in_place(lib):
+    # y aliasing x: the down pass runs unsplit, so x is intact while the
+    # gate/up pass reads it
+    m, hidden, inter = 4, 1024, 4096
+    say("ffn decode in place 1024/4096 m=4")
+    wg, wu, wd = synth.dense_ffn_weights(97, hidden, inter)
+    x = synth.activations(97, m, hidden, outliers=True)
+    buf = dev(x)
+    lib.ffn_swiglu_q4k(dev(wg), dev(wu), dev(wd), buf, lib.Q4K_F32, m, hidden, inter, buf,
+                       workspace(lib, m, hidden, inter))
+    assert orc.relative_l2(host(buf), orc.ffn_decode(wg, wu, wd, hidden, inter, x)) <= TOL
+
+
 @pytest.mark.parametrize("m", [1, 4, 8])
 def test_decode_q8_ffn_7b(lib, decode7b, m):
     # Q8_1 decode regime: the prefill arithmetic (Q8_1 of x and of h) on the
