@@ -42,10 +42,10 @@ ROTATE_BYTES = 1 << 30         # per rotated tensor set
 # WRITE_SIZE (each scaled by what it reads for a copy of known size; summary and commands in
 # profiles/gemv_d4_decode_sweep_hbm_traffic.md) for the kernel sources with these SHA-256
 # digests.  Reported only while the sources still match.
-TRAFFIC_SWEEP_BYTES = 61134272
+TRAFFIC_SWEEP_BYTES = 61115808
 TRAFFIC_SOURCES = {
     "gemm_block_q4_amd/csrc/gemv_valu.hip":
-        "24b1babb3e81b245208873f972c416fa1e84ca3f2775a593efa4e31554483a3e",
+        "5bac50afe4bac95be2feaf0bd626334dda4c772bd2370ba036a288cf7766f3b1",
     "gemm_block_q4_amd/csrc/slice_dot.hpp":
         "2537bd57a417fc0675d828787fd917af1b119de52e1be70ef9f0d7168421d428",
     "gemm_block_q4_amd/csrc/lane_reduce.hpp":
@@ -58,7 +58,7 @@ TRAFFIC_SOURCES = {
 # the kernel the roofline describes (one token, dense): layout 1 (a row is one
 # wavefront) for k = 4096, layout 2 (a row spans wavefronts) for k = 11008
 GEMV_KERNEL = ("gemv_d4_kernel<false, false, 0, 1, 1, 4> for k = 4096 and "
-               "gemv_d4_kernel<false, false, 0, 2, 2, 2> for k = 11008 (q4k_gemv, m = 1)")
+               "gemv_d4_kernel<false, false, 0, 2, 1, 2> for k = 11008 (q4k_gemv, m = 1)")
 
 
 def log(*a):

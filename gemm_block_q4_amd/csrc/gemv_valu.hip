@@ -553,11 +553,15 @@ hipError_t launch_mode(const GemvArgs& a, hipStream_t stream) {
   const size_t lds = lds_bytes(geo, a.k, GU);
   if (geo.rows < geo.step || lds > kLdsMax) return hipErrorInvalidValue;
   // activation units (16 values) per thread: one when a row fits a wavefront
-  // (at most 256 units for 256 threads), else two or four (k <= 32768 keeps
-  // units <= 4 * threads for every row width)
+  // (at most 256 units for 256 threads), else one, two or four (k <= 32768
+  // keeps units <= 4 * threads for every row width).  The fewest that cover
+  // the units: a unit past the end still issues its (zero-returning) loads,
+  // which queue ahead of the weight loads (k = 11008 on 12 wavefronts: 688
+  // units, one per thread, 7.6 us against 8.1 with two).
   const int units = 16 * (a.k / kQK);
   const int nthr = geo.waves * 64;
   if (geo.wr > 1) {
+    if (units <= nthr) return launch_layout<GU, BF16, MODE, kWide, 1>(a, geo, lds, grid_y, stream);
     if (units <= 2 * nthr) return launch_layout<GU, BF16, MODE, kWide, 2>(a, geo, lds, grid_y, stream);
     if (units <= 4 * nthr) return launch_layout<GU, BF16, MODE, kWide, 4>(a, geo, lds, grid_y, stream);
     return hipErrorInvalidValue;
