@@ -15,32 +15,52 @@ namespace q4k {
 
 namespace {
 
+// y[t][c] = sum over the valid slots s of wts[t][s] * y_pair[t * top_k + s][c],
+// in slot order.  VEC: four consecutive columns per thread (16-byte loads and
+// stores; hidden % 4 == 0 and 16-byte aligned rows), else one.
+template <bool VEC>
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ y_pair,
                                                           const float* __restrict__ wts,
                                                           const int32_t* __restrict__ ids,
                                                           int m, int top_k, int n_experts,
                                                           int hidden, float* __restrict__ y) {
+  constexpr int V = VEC ? 4 : 1;
   const int t = blockIdx.y;
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * V;
   if (t >= m || c >= hidden) return;
   // eight slots per round: all their loads are issued (on clamped, valid
   // indices) before the first is used; the sum stays in slot order
-  float acc = 0.f;
+  float acc[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) acc[j] = 0.f;
   for (int s0 = 0; s0 < top_k; s0 += 8) {
-    int e[8];
-    float w[8], v[8];
+    bool ok[8];
+    float w[8], v[8][V];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int p = t * top_k + min(s0 + i, top_k - 1);
       const int id = ids[p];
-      e[i] = s0 + i < top_k ? id : -1;
+      ok[i] = s0 + i < top_k && id >= 0 && id < n_experts;
       w[i] = wts[p];
-      v[i] = y_pair[static_cast<size_t>(p) * hidden + c];
+      const float* src = y_pair + static_cast<size_t>(p) * hidden + c;
+      if constexpr (VEC) {
+        const float4 q = *reinterpret_cast<const float4*>(src);
+        v[i][0] = q.x; v[i][1] = q.y; v[i][2] = q.z; v[i][3] = q.w;
+      } else {
+        v[i][0] = *src;
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc = e[i] >= 0 && e[i] < n_experts ? fmaf(w[i], v[i], acc) : acc;
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < V; ++j) acc[j] = ok[i] ? fmaf(w[i], v[i][j], acc[j]) : acc[j];
   }
-  y[static_cast<size_t>(t) * hidden + c] = acc;
+  float* dst = y + static_cast<size_t>(t) * hidden + c;
+  if constexpr (VEC) {
+    *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  } else {
+    *dst = acc[0];
+  }
 }
 
 // One workgroup: per-expert pair counts by LDS atomics, an exclusive scan of
@@ -116,9 +136,15 @@ __global__ __launch_bounds__(1024) void moe_route_kernel(const int32_t* __restri
 hipError_t launch_moe_combine(const float* y_pair, const float* wts, const int32_t* ids, int m,
                               int top_k, int n_experts, int hidden, float* y,
                               hipStream_t stream) {
-  const dim3 grid((hidden + 255) / 256, m);
-  moe_combine_kernel<<<grid, dim3(256), 0, stream>>>(y_pair, wts, ids, m, top_k, n_experts,
-                                                     hidden, y);
+  const bool vec = hidden % 4 == 0 && reinterpret_cast<uintptr_t>(y_pair) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(y) % 16 == 0;
+  if (vec) {
+    const dim3 grid((hidden / 4 + 255) / 256, m);
+    moe_combine_kernel<true><<<grid, dim3(256), 0, stream>>>(y_pair, wts, ids, m, top_k, n_experts, hidden, y);
+  } else {
+    const dim3 grid((hidden + 255) / 256, m);
+    moe_combine_kernel<false><<<grid, dim3(256), 0, stream>>>(y_pair, wts, ids, m, top_k, n_experts, hidden, y);
+  }
   return hipGetLastError();
 }
 
