@@ -42,7 +42,6 @@
 // chunk's activations are in flight while the current ones are multiplied,
 // and reductions across lanes use DPP.  The W partial tiles are added in a
 // fixed order at the end (deterministic).
-#include <algorithm>
 #include <type_traits>
 
 #include "q4k_device.hpp"
