@@ -69,12 +69,21 @@ template <int MT> constexpr int chunk_blocks() { return 2; }
 //   op: [CH][8 steps][4 lane groups][R2 rows] x 8 halves (16 B per entry);
 //       rows 0..HR-1 hold the hi halves of the tokens, rows HR..R2-1 the lo
 //   shift: [8] exponent sh per token (one per chunk)
+// The lane-group and step strides are padded (R2 = 8: a step is 33 entries;
+// R2 = 16: a lane group 17, a step 68) so that one token's 8-byte conversion
+// writes (all steps and lane groups at once) fall at most two to a bank; with
+// strides that are multiples of 256 bytes all eight steps hit the same banks
+// (counters showed 60-75% of the LDS cycles as bank conflicts).  A step's
+// operand reads stay one contiguous run per lane group.
 template <int MT>
 struct WaveLds {
   static constexpr int kCH = chunk_blocks<MT>();
   static constexpr int kR2 = 2 * half_rows<MT>();
-  uint4 op[kCH * 8 * 4 * kR2];
+  static constexpr int kSG = kR2 == 16 ? kR2 + 1 : kR2;           // lane-group stride (entries)
+  static constexpr int kSS = kR2 == 16 ? 4 * kSG : 4 * kSG + 1;   // step stride (entries)
+  uint4 op[kCH * 8 * kSS];
   int shift[8];
+  __device__ static int idx(int bi, int s, int g, int row) { return (bi * 8 + s) * kSS + g * kSG + row; }
 };
 
 template <int MT, bool GU, int W>
@@ -245,7 +254,7 @@ __device__ __forceinline__ void convert_chunk(WaveLds<MT>& L, const XT (&xv)[MT]
       const uint32_t h01 = pkrtz(v0, v1), h23 = pkrtz(v2, v3);
       const uint32_t l01 = pkrtz(v0 - lo_half(h01), v1 - hi_half(h01));
       const uint32_t l23 = pkrtz(v2 - lo_half(h23), v3 - hi_half(h23));
-      const int e = ((bi * 8 + s) * 4 + g) * R2 + t;
+      const int e = WaveLds<MT>::idx(bi, s, g, t);
       reinterpret_cast<uint2*>(&L.op[e])[half] = make_uint2(h01, h23);
       reinterpret_cast<uint2*>(&L.op[e + HR])[half] = make_uint2(l01, l23);
     }
@@ -313,7 +322,7 @@ __device__ __forceinline__ void block_mfma(const BlockRegs& r, int g, const Wave
   for (int s = 0; s < 8; ++s) {
     const v8h b = s < 4 ? weights8(w[2 * s], w[2 * s + 1], s0, o0)
                         : weights8(w[2 * (s - 4)] >> 4, w[2 * (s - 4) + 1] >> 4, s1, o1);
-    const v8h av = __builtin_bit_cast(v8h, L.op[((bi * 8 + s) * 4 + g) * R2 + arow]);
+    const v8h av = __builtin_bit_cast(v8h, L.op[WaveLds<MT>::idx(bi, s, g, arow)]);
     cm = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b, cm, 0, 0, 0);
     cn = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, s < 4 ? bm0 : bm1, cn, 0, 0, 0);
   }

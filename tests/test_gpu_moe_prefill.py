@@ -113,3 +113,21 @@ def test_moe_prefill_many_experts(lib):
     y = moe_prefill_gpu(lib, banks, x, ids, wts, n_exp, hidden, inter)
     ref = orc.moe_prefill(*banks, n_exp, hidden, inter, x, ids, wts)
     assert orc.relative_l2(y, ref) <= TOL
+
+
+def test_moe_prefill_output_not_16_byte_aligned(lib):
+    # y one float past a 16-byte boundary: the combine takes its
+    # one-column-per-thread form
+    n_exp, hidden, inter, m, k = 5, 256, 256, 20, 2
+    say("moe prefill, y offset by one float")
+    banks = synth.moe_banks(94, n_exp, hidden, inter)
+    x = synth.activations(94, m, hidden, outliers=True)
+    ids, wts = synth.router(94, m, n_exp, k)
+    buf = empty((m * hidden + 1,), torch.float32)
+    y = buf[1:].view(m, hidden)
+    bg, bu, bd = banks
+    lib.ffn_swiglu_q4k(dev(bg), dev(bu), dev(bd), dev(x), lib.Q4K_F32, m, hidden, inter, y,
+                       workspace(lib, m, hidden, inter, k, 0), n_experts=n_exp, ids=dev(ids),
+                       wts=dev(wts), top_k=k)
+    ref = orc.moe_prefill(*banks, n_exp, hidden, inter, x, ids, wts)
+    assert orc.relative_l2(host(y), ref) <= TOL
