@@ -42,10 +42,10 @@ ROTATE_BYTES = 1 << 30         # per rotated tensor set
 # WRITE_SIZE (each scaled by what it reads for a copy of known size; summary and commands in
 # profiles/gemv_d4_decode_sweep_hbm_traffic.md) for the kernel sources with these SHA-256
 # digests.  Reported only while the sources still match.
-TRAFFIC_SWEEP_BYTES = 61115808
+TRAFFIC_SWEEP_BYTES = 61117852
 TRAFFIC_SOURCES = {
     "gemm_block_q4_amd/csrc/gemv_valu.hip":
-        "5bac50afe4bac95be2feaf0bd626334dda4c772bd2370ba036a288cf7766f3b1",
+        "17a03dc5cb645b393d6de1bc386efa643139a3b66631c8900087756d6e6eb327",
     "gemm_block_q4_amd/csrc/slice_dot.hpp":
         "2537bd57a417fc0675d828787fd917af1b119de52e1be70ef9f0d7168421d428",
     "gemm_block_q4_amd/csrc/lane_reduce.hpp":

@@ -188,9 +188,18 @@ __global__ __launch_bounds__(LAYOUT == kWide ? kThreadsMax : kThreadsNarrow) voi
     // 1. this thread's activation units, loaded before any weight
     float4 xr[XU][4];
 #pragma unroll
-    for (int j = 0; j < XU; ++j)
+    for (int j = 0; j < XU; ++j) {
+      // a wavefront whose units all lie past the end issues no loads (a
+      // uniform branch; zero-returning loads would still take texture-path
+      // slots ahead of the weights)
+      if (wave * 64 + j * nthr < units) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) xr[j][c] = load_x4<BF16>(rx, unit_off(tid + j * nthr, c));
+        for (int c = 0; c < 4; ++c) xr[j][c] = load_x4<BF16>(rx, unit_off(tid + j * nthr, c));
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) xr[j][c] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
 
     // Every wavefront issues its activation loads before any weight load:
     // the compute unit's texture path (64 B/clk) serves loads roughly in
