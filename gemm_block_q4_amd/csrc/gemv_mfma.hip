@@ -69,18 +69,19 @@ template <int MT> constexpr int chunk_blocks() { return 2; }
 //   op: [CH][8 steps][4 lane groups][R2 rows] x 8 halves (16 B per entry);
 //       rows 0..HR-1 hold the hi halves of the tokens, rows HR..R2-1 the lo
 //   shift: [8] exponent sh per token (one per chunk)
-// The lane-group and step strides are padded (R2 = 8: a step is 33 entries;
-// R2 = 16: a lane group 17, a step 68) so that one token's 8-byte conversion
-// writes (all steps and lane groups at once) fall at most two to a bank; with
-// strides that are multiples of 256 bytes all eight steps hit the same banks
-// (counters showed 60-75% of the LDS cycles as bank conflicts).  A step's
-// operand reads stay one contiguous run per lane group.
+// The step stride is padded by one entry (4 R2 + 1) so that one token's
+// 8-byte conversion writes (all steps and lane groups at once) spread over the
+// banks; with a stride of 4 R2 entries, a multiple of 256 bytes, all eight
+// steps hit the same banks (counters: 60-80% of the LDS cycles were bank
+// conflicts, 1-7% with the pad; at eight tokens, padding the lane-group
+// stride as well, by one or two entries, left 60-80%).  A step's operand
+// reads stay one contiguous run per lane group.
 template <int MT>
 struct WaveLds {
   static constexpr int kCH = chunk_blocks<MT>();
   static constexpr int kR2 = 2 * half_rows<MT>();
-  static constexpr int kSG = kR2 == 16 ? kR2 + 1 : kR2;           // lane-group stride (entries)
-  static constexpr int kSS = kR2 == 16 ? 4 * kSG : 4 * kSG + 1;   // step stride (entries)
+  static constexpr int kSG = kR2;          // lane-group stride (entries)
+  static constexpr int kSS = 4 * kSG + 1;  // step stride (entries)
   uint4 op[kCH * 8 * kSS];
   int shift[8];
   __device__ static int idx(int bi, int s, int g, int row) { return (bi * 8 + s) * kSS + g * kSG + row; }
