@@ -127,7 +127,8 @@ struct FStage {
 // k values 32 (l / 32) .. +31 of its A row and its B row (the instruction
 // pairs A and B bytes by the same lane half and byte position).
 // Staging: k advances by 128 per stage through two LDS buffers; the global
-// loads of stage s + 2 are in flight while stage s is multiplied.  Tokens past
+// loads of stages s + 1 and s + 2 are in flight in two register sets while
+// stage s is multiplied.  Tokens past
 // m, weight rows past n and k past the end read zeros (raw buffer bounds and
 // kOob offsets), which add nothing.
 template <int WM>
@@ -159,8 +160,12 @@ __global__ __launch_bounds__(128 * WM) void fp8_gemm_kernel(const uint8_t* __res
   const int scol = 16 * (tid % kFCh);
   const int srow0 = tid / kFCh;
   constexpr int kRowStep = kThreads / kFCh;
-  uint4 la[kAChunks], lw[kWChunks];
-  auto load = [&](int s) {
+  // two register sets of staging loads: the loads of stage s + 3 are issued
+  // while stage s + 1 waits in the other set for its LDS store, so every
+  // load has two stages of compute to arrive (one set held one stage, short
+  // of the L2 / HBM latency at these rates)
+  uint4 la0[kAChunks], lw0[kWChunks], la1[kAChunks], lw1[kWChunks];
+  auto load = [&](int s, uint4 (&la)[kAChunks], uint4 (&lw)[kWChunks]) {
     const int col = s * kFK + scol;
     const bool in = col < k;
 #pragma unroll
@@ -170,7 +175,7 @@ __global__ __launch_bounds__(128 * WM) void fp8_gemm_kernel(const uint8_t* __res
     for (int i = 0; i < kWChunks; ++i)
       lw[i] = buf_load16(rw, in ? static_cast<uint32_t>(srow0 + kRowStep * i) * k + col : kOob);
   };
-  auto store = [&](Stage& S) {
+  auto store = [&](Stage& S, const uint4 (&la)[kAChunks], const uint4 (&lw)[kWChunks]) {
 #pragma unroll
     for (int i = 0; i < kAChunks; ++i)
       *reinterpret_cast<uint4*>(&S.a[(srow0 + kRowStep * i) * kFStride + scol]) = la[i];
@@ -186,13 +191,7 @@ __global__ __launch_bounds__(128 * WM) void fp8_gemm_kernel(const uint8_t* __res
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[ti][wt][i] = 0.f;
   const int r32 = lane & 31, kh = lane >> 5;
-  const int nst = (k + kFK - 1) / kFK;
-  load(0);
-  store(st[0]);
-  if (nst > 1) load(1);
-  __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    const Stage& S = st[s & 1];
+  auto compute = [&](const Stage& S) {
 #pragma unroll
     for (int ks = 0; ks < kFK / 64; ++ks) {
       const int kb = ks * 64 + 32 * kh;
@@ -207,12 +206,27 @@ __global__ __launch_bounds__(128 * WM) void fp8_gemm_kernel(const uint8_t* __res
         for (int wt = 0; wt < 2; ++wt)
           acc[ti][wt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[ti], bv[wt], acc[ti][wt], 0, 0, 0, 0, 0, 0);
     }
-    if (s + 1 < nst) {
-      // stage s + 1 goes to the buffer stage s - 1 used (every wavefront left
-      // it at the previous barrier); then the loads of stage s + 2
-      store(st[(s + 1) & 1]);
-      if (s + 2 < nst) load(s + 2);
-    }
+  };
+  // Stage s is in LDS buffer s & 1; stage s + 1 waits in one register set,
+  // stage s + 2 is in flight in the other.  No load is conditional: stages
+  // past k read zeros (an odd stage count runs one stage of zeros, which adds
+  // exact zeros), so the compiler can count the loads in flight.
+  const int nst = (k + kFK - 1) / kFK;
+  load(0, la0, lw0);
+  store(st[0], la0, lw0);
+  load(1, la1, lw1);
+  load(2, la0, lw0);
+  __syncthreads();
+  for (int s = 0; s < nst; s += 2) {
+    compute(st[0]);
+    // stage s + 1 to the buffer stage s - 1 used (every wavefront left it at
+    // the previous barrier), then the loads of stage s + 3
+    store(st[1], la1, lw1);
+    load(s + 3, la1, lw1);
+    __syncthreads();
+    compute(st[1]);
+    store(st[0], la0, lw0);
+    load(s + 4, la0, lw0);
     __syncthreads();
   }
   // epilogue: D rounded to bfloat16 (nearest even) and widened, times the
