@@ -120,6 +120,36 @@ def test_decode_ffn_split_down(lib, m, hidden, inter):
         assert orc.relative_l2(host(y), orc.ffn_decode(wg, wu, wd, hidden, inter, x)) <= TOL
 
 
+def _scale_rows(w, rows, k, factor):
+    """Multiply d and dmin of every block of the given rows by a power of two."""
+    blk = w.reshape(-1, k // 256, 144)
+    for r in rows:
+        for off in (0, 2):
+            h = blk[r, :, off:off + 2].copy().view(np.float16)
+            blk[r, :, off:off + 2] = (h.astype(np.float32) * factor).astype(np.float16).view(np.uint8)
+
+
+def test_decode_ffn_split_uneven_magnitudes(lib):
+    # h with uneven magnitudes on the split down pass, whose activation scale
+    # is per (token, chunk of 512 values): all-zero rows (gate rows 0..31
+    # without scale), 16 rows 2^12 above the rest of their chunk (up rows
+    # 64..79), 16 rows 2^-10 below (up rows 1024..1039), and a token whose x
+    # and hence h are all zero (y exactly zero)
+    m, hidden, inter = 3, 1024, 4096
+    say("ffn decode split down, uneven magnitudes 1024/4096 m=3")
+    wg, wu, wd = synth.dense_ffn_weights(98, hidden, inter)
+    _scale_rows(wg, range(0, 32), hidden, 0.0)
+    _scale_rows(wu, range(64, 80), hidden, 2.0 ** 12)
+    _scale_rows(wu, range(1024, 1040), hidden, 2.0 ** -10)
+    x = synth.activations(98, m, hidden, outliers=True)
+    x[1] = 0.0
+    y = ffn_gpu(lib, wg, wu, wd, x, hidden, inter)
+    ref = orc.ffn_decode(wg, wu, wd, hidden, inter, x)
+    assert np.all(y[1] == 0.0)
+    for t in (0, 2):
+        assert orc.relative_l2(y[t], ref[t]) <= TOL
+
+
 def test_decode_ffn_in_place(lib):
     # y aliasing x: the down pass runs unsplit, so x is intact while the
     # gate/up pass reads it
