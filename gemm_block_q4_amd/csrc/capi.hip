@@ -122,9 +122,10 @@ struct FfnLayout {
   size_t total = 0;
   // decode dense (and MoE: h and the pair outputs of every (token, slot) pair)
   size_t h = 0, y_pair = 0;
-  // prefill and decode_q8: Q8_1 of x and of h, and h itself (decode_q8; the
-  // prefill pass leaves it unwritten, and the span qx .. qh holds the
-  // prefill down pass's k-split partial sums)
+  // prefill and decode_q8: Q8_1 of x and of h, and h itself (decode_q8; in
+  // the prefill regime the span of h holds the k-split gate/up sums of the
+  // fused pass's last row tiles, and the span qx .. qh the down pass's
+  // k-split partial sums)
   size_t qx = 0, dx = 0, qh = 0, dh = 0;
   // MoE prefill: the pairs sorted by expert, the tile table and its count
   // (qh, dh: Q8_1(h) of the pairs in sorted order; y_pair: pair outputs)
@@ -671,6 +672,40 @@ int ffn_common(const void* w_gate, const void* w_up, const void* w_down, int n_e
   gu.m = m;
   gu.n = inter;
   gu.k = hidden;
+  // The fused pass runs (inter/64) x ceil(m/128) workgroups, one per compute
+  // unit at a time.  When its last round would leave compute units idle
+  // (512 tokens at 5120/17408: 1088 workgroups, 4.25 rounds on 256 CUs), the
+  // last row tiles run first as a k-split pass that fills one round, whose
+  // gate and up sums go to the span of h (not read by this FFN's passes
+  // before the down pass overwrites it) and are added in split order by a
+  // small kernel that applies silu * mul and writes their Q8_1(h); the other
+  // row tiles then run as before.
+  const int cus = device_cus();
+  const int rt = inter / 64, tt = (m + 127) / 128;
+  const long long gu_tiles = static_cast<long long>(rt) * tt;
+  int tail = 0, tsplit = 1;
+  if (cus > 0 && gu_tiles > cus && gu_tiles % cus != 0) {
+    tail = static_cast<int>((gu_tiles % cus + tt - 1) / tt);
+    tsplit = std::min({4, hidden / Q4K_QK, cus / (tail * tt), rt / (2 * tail)});
+    if (tsplit < 2) tail = 0;
+  }
+  if (tail > 0) {
+    float* parts = h;
+    MmqArgs tp = gu;
+    tp.y = nullptr;
+    tp.q_out = nullptr;
+    tp.d_out = nullptr;
+    tp.gu_parts = parts;
+    tp.row_tile0 = rt - tail;
+    tp.row_tiles = tail;
+    tp.splits = tsplit;
+    tp.split_blocks = (hidden / Q4K_QK + tsplit - 1) / tsplit;
+    if ((e = launch_mmq(tp, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
+    if ((e = launch_mmq_gu_finish(parts, tsplit, m, tail * 64, (rt - tail) * 64, inter, qh, dh, s)) !=
+        hipSuccess)
+      return Q4K_ERR_LAUNCH;
+    gu.row_tiles = rt - tail;
+  }
   if ((e = launch_mmq(gu, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
   MmqArgs dn{};
   dn.w = static_cast<const uint8_t*>(w_down);
@@ -684,7 +719,6 @@ int ffn_common(const void* w_gate, const void* w_up, const void* w_down, int n_e
   // k range; the partial sums go to the span of qx, dx and h, which the down
   // pass does not read, and are added in split order.
   const size_t plane = static_cast<size_t>(m) * static_cast<size_t>(hidden);
-  const int cus = device_cus();
   const int max_splits = static_cast<int>(std::min<size_t>((L.qh - L.qx) / (plane * 4), 8));
   const int splits = cus > 0 && max_splits > 1 && aligned(y, 16)  // the reduction stores float4
                          ? mmq_choose_splits(m, hidden, inter, max_splits, cus)

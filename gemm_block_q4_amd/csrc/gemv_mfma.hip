@@ -298,7 +298,6 @@ __device__ __forceinline__ void load_block(rsrc_t r, uint32_t off, int g, BlockR
 template <int MT>
 __device__ __forceinline__ void block_mfma(const BlockRegs& r, int g, const WaveLds<MT>& L, int bi,
                                            int arow, float& d, float& dmin, v4f& cm, v4f& cn) {
-  constexpr int R2 = WaveLds<MT>::kR2;
   d = half_bits_to_float(r.h.x & 0xFFFFu);
   dmin = half_bits_to_float(r.h.x >> 16);
   uint32_t sc0, mn0, sc1, mn1;

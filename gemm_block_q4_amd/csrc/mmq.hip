@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;  // wm 0..3: token tile; wn 0..1: weight half
-  const int n0 = blockIdx.x * RPM;
+  const int n0 = (static_cast<int>(blockIdx.x) + a.row_tile0) * RPM;
   const int K = a.k / kQK;
   const int nsub = a.k / kSub;
   const int rows = min(RPM, a.n - n0);
@@ -448,7 +448,24 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
   }
 
   if constexpr (GU && !PARTIALS) {
-    if (a.q_out != nullptr) {  // uniform
+    if (a.gu_parts != nullptr) {  // uniform: a k split of the fused pass
+      // gate and up sums of this split, rows wn*32 + 8*(i/4) + 4*kh + i%4
+      if (xtok < toks) {
+        const size_t ld = static_cast<size_t>(a.row_tiles) * RPM;
+        const size_t tok = static_cast<size_t>(t0 + xtok);
+        const size_t r0 = static_cast<size_t>(n0 - a.row_tile0 * RPM);
+        float* pg = a.gu_parts + (static_cast<size_t>(2 * blockIdx.z) * a.m + tok) * ld + r0;
+        float* pu = pg + static_cast<size_t>(a.m) * ld;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = wn * 32 + 8 * (i >> 2) + 4 * kh + (i & 3);
+          if (r < rows) {
+            pg[r] = acc[0][i] - accm[0][i];
+            pu[r] = acc[1][i] - accm[1][i];
+          }
+        }
+      }
+    } else if (a.q_out != nullptr) {  // uniform
       // Lanes l and l + 32 hold rows wn*32 + 8*(i/4) + 4*kh + i%4 of token
       // xtok: together the 32 values of one Q8_1 block of h (n0 + wn*32 is a
       // multiple of 32 and every row exists, n % 64 == 0).
@@ -485,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
       const int orow = GRP && a.group_scatter ? a.group_list[t0 + xtok] : t0 + xtok;
       const size_t roff = blockIdx.z * a.split_stride + static_cast<size_t>(orow) * a.n;
       if constexpr (GU) {
-        if (a.q_out == nullptr) {
+        if (a.q_out == nullptr && a.gu_parts == nullptr) {
           float* yrow = a.y + roff;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
@@ -520,7 +537,8 @@ __global__ __launch_bounds__(kThreads) void mmq_kernel(MmqArgs a) {
 template <bool GU, bool PARTIALS, bool GRP = false, bool GATHER = false>
 hipError_t launch(const MmqArgs& a, hipStream_t stream) {
   constexpr int RPM = Geometry<GU>::kRowsPerMatrix;
-  const dim3 grid((a.n + RPM - 1) / RPM, GRP ? a.group_grid_rows : (a.m + kBM - 1) / kBM, a.splits);
+  const dim3 grid(a.row_tiles > 0 ? a.row_tiles : (a.n + RPM - 1) / RPM,
+                  GRP ? a.group_grid_rows : (a.m + kBM - 1) / kBM, a.splits);
   const size_t lds = 2 * sizeof(Stage);
   auto kern = mmq_kernel<GU, PARTIALS, GRP, GATHER>;
   const hipError_t e = lds_opt_in(reinterpret_cast<const void*>(kern), lds);
@@ -536,7 +554,15 @@ hipError_t launch_mmq(const MmqArgs& args, hipStream_t stream) {
   const int K = a.k / kQK;
   if (a.q_out && (!a.w_up || !a.d_out || a.partials || a.n % 64)) return hipErrorInvalidValue;
   if (a.y_bf16 && (a.w_up || a.partials || a.splits > 1)) return hipErrorInvalidValue;
-  if (a.splits <= 1 || a.w_up || a.partials) {
+  if (a.row_tile0 < 0 || a.row_tiles < 0 || (a.row_tiles == 0 && a.row_tile0 != 0) || a.group_tiles ||
+      a.partials) {
+    if (a.row_tile0 != 0 || a.row_tiles != 0 || a.gu_parts) return hipErrorInvalidValue;
+  } else if (a.row_tiles > 0) {
+    const int rpm = a.w_up ? 64 : 128;
+    if (a.row_tile0 + a.row_tiles > (a.n + rpm - 1) / rpm) return hipErrorInvalidValue;
+  }
+  if (a.gu_parts && (!a.w_up || a.q_out || a.row_tiles < 1)) return hipErrorInvalidValue;
+  if (a.splits <= 1 || (a.w_up && !a.gu_parts) || a.partials) {
     a.splits = 1;
     a.split_blocks = K;
     a.split_stride = 0;
@@ -597,7 +623,48 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
   reinterpret_cast<float4*>(y)[i] = acc;
 }
 
+// One 32-lane half of a wavefront per (token, 32-row block of h).
+__global__ __launch_bounds__(256) void gu_finish_kernel(const float* __restrict__ parts, int splits, int m,
+                                                        int rows, int row0, int n, int8_t* __restrict__ q_out,
+                                                        uint32_t* __restrict__ d_out) {
+  const int blk = static_cast<int>(blockIdx.x) * 8 + static_cast<int>(threadIdx.x >> 5);
+  const int nblk = rows / 32;
+  if (blk >= m * nblk) return;  // uniform in the half wavefront
+  const int t = blk / nblk;
+  const int r = (blk - t * nblk) * 32 + static_cast<int>(threadIdx.x & 31);
+  const size_t plane = static_cast<size_t>(m) * rows;
+  const size_t at = static_cast<size_t>(t) * rows + r;
+  float g = 0.f, u = 0.f;
+  for (int z = 0; z < splits; ++z) {
+    g += parts[2 * z * plane + at];
+    u += parts[(2 * z + 1) * plane + at];
+  }
+  const float hv = silu_mul(g, u);
+  float amax = fabsf(hv);
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+  const float d = q8_1_scale(amax);
+  const int q = q8_1_quant(hv, amax, d);
+  int sum = q;
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 32);
+  const size_t row = static_cast<size_t>(row0) + r;
+  q_out[static_cast<size_t>(t) * n + row] = static_cast<int8_t>(q);
+  if ((threadIdx.x & 31) == 0) d_out[static_cast<size_t>(t) * (n / 32) + row / 32] = q8_1_word(amax, d, sum);
+}
+
 }  // namespace
+
+hipError_t launch_mmq_gu_finish(const float* parts, int splits, int m, int rows, int row0, int n,
+                                int8_t* q_out, uint32_t* d_out, hipStream_t stream) {
+  if (splits < 1 || m < 1 || rows < 32 || rows % 32 || row0 % 32 || n % 32 || row0 + rows > n)
+    return hipErrorInvalidValue;
+  const long long blocks = (static_cast<long long>(m) * (rows / 32) + 7) / 8;
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  gu_finish_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(parts, splits, m, rows, row0, n,
+                                                                                   q_out, d_out);
+  return hipGetLastError();
+}
 
 hipError_t launch_mmq_split_reduce(const float* parts, int splits, size_t stride, size_t count,
                                    float* y, hipStream_t stream) {

@@ -106,9 +106,25 @@ struct MmqArgs {
   int group_top_k;
   int group_scatter;
   int group_grid_rows;
+  // Dense passes over part of the rows: row tiles [row_tile0, row_tile0 +
+  // row_tiles) of the workgroup's row count (64 per matrix in the fused
+  // gate/up pass); row_tiles 0: all rows.
+  int row_tile0, row_tiles;
+  // Fused gate/up pass with a k split (splits > 1, split_blocks as above):
+  // split z writes its gate and up sums (before silu * mul) to the planes
+  // gu_parts [z][2][m][row_tiles * 64], rows counted from row_tile0 * 64;
+  // launch_mmq_gu_finish adds them in split order and writes Q8_1(h).
+  float* gu_parts;
 };
 
 hipError_t launch_mmq(const MmqArgs& a, hipStream_t stream);
+
+// Q8_1(silu(g) * u) of rows [row0, row0 + rows) of an [m][n] h from the
+// planes of a k-split fused gate/up pass (parts [splits][2][m][rows]), the
+// splits added in order; the quantisation arithmetic of the fused epilogue.
+// rows and row0 are multiples of 32.
+hipError_t launch_mmq_gu_finish(const float* parts, int splits, int m, int rows, int row0, int n,
+                                int8_t* q_out, uint32_t* d_out, hipStream_t stream);
 
 // Q8_1-activation decode GEMV: y [m][n] = reference dot of Q8_1 rows with the
 // Q4_K rows, 1 <= m <= 8, 256 <= k <= 32768 (validated by the caller).

@@ -188,6 +188,24 @@ def test_decode_q8_ffn_shapes(lib, m, hidden, inter, bf16):
     assert np.all(np.isfinite(y))
 
 
+@pytest.mark.parametrize("m,hidden", [(130, 512), (300, 1024)])
+def test_prefill_ffn_gate_up_tail_split(lib, m, hidden):
+    # 272 row tiles of the fused gate/up pass x 2 or 3 token tiles leave a
+    # partial last round on 256 compute units: the last 16 row tiles run as a
+    # k-split pass (2 and 4 splits, the last token tile ragged) whose gate and
+    # up sums are added by the finishing kernel; every fifth token (every
+    # lane position of a token tile over the sample) and the last are compared
+    inter = 17408
+    tokens = sorted(set(range(0, m, 5)) | {m - 1})
+    say(f"ffn prefill gate/up tail split {hidden}/{inter} m={m}")
+    wg, wu, wd = synth.dense_ffn_weights(92, hidden, inter)
+    x = synth.activations(92, m, hidden, outliers=True, sub=m)
+    y = ffn_gpu(lib, wg, wu, wd, x, hidden, inter, bf16=True)
+    xb = synth.bf16_bits_to_f32(synth.to_bf16_bits(x))
+    ref = orc.ffn_prefill(wg, wu, wd, hidden, inter, xb, tokens=tokens)
+    assert orc.relative_l2(y[tokens], ref) <= TOL
+
+
 @pytest.fixture(scope="module")
 def prefill_weights():
     return synth.dense_ffn_weights(synth.PREFILL_FFN, 5120, 17408)
