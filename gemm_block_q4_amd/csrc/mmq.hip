@@ -554,13 +554,14 @@ hipError_t launch_mmq(const MmqArgs& args, hipStream_t stream) {
   const int K = a.k / kQK;
   if (a.q_out && (!a.w_up || !a.d_out || a.partials || a.n % 64)) return hipErrorInvalidValue;
   if (a.y_bf16 && (a.w_up || a.partials || a.splits > 1)) return hipErrorInvalidValue;
-  if (a.row_tile0 < 0 || a.row_tiles < 0 || (a.row_tiles == 0 && a.row_tile0 != 0) || a.group_tiles ||
-      a.partials) {
-    if (a.row_tile0 != 0 || a.row_tiles != 0 || a.gu_parts) return hipErrorInvalidValue;
-  } else if (a.row_tiles > 0) {
+  // a range of row tiles: dense passes only, inside the matrix
+  if (a.row_tiles != 0 || a.row_tile0 != 0) {
     const int rpm = a.w_up ? 64 : 128;
-    if (a.row_tile0 + a.row_tiles > (a.n + rpm - 1) / rpm) return hipErrorInvalidValue;
+    if (a.group_tiles || a.partials || a.row_tiles < 1 || a.row_tile0 < 0 ||
+        a.row_tile0 + a.row_tiles > (a.n + rpm - 1) / rpm)
+      return hipErrorInvalidValue;
   }
+  // k-split sums of the fused pass: over a range of row tiles, no epilogue
   if (a.gu_parts && (!a.w_up || a.q_out || a.row_tiles < 1)) return hipErrorInvalidValue;
   if (a.splits <= 1 || (a.w_up && !a.gu_parts) || a.partials) {
     a.splits = 1;
