@@ -86,6 +86,17 @@ def test_mmq_prefill_gate_full_size(lib):
     assert np.array_equal(y1, y2)
 
 
+def test_mmq_down_shape_2048_tokens(lib):
+    # the single-matrix MMQ as measured: [5120, 17408] at 2048 tokens (40 x 16
+    # workgroups), one token from every 128-token tile and the last
+    n, k, m = 5120, 17408, 2048
+    say(f"mmq full size m={m} n={n} k={k} (sampled tokens)")
+    w = synth.random_q4k(synth.rng(86, 1), n, k)
+    qs, d16, s = quantised(m, k, 11, bf16=True)
+    tokens = sorted({128 * i + (53 * i + 11) % 128 for i in range(m // 128)} | {m - 1})
+    check(lib, w, qs, d16, s, n, k, tokens=tokens)
+
+
 def test_mmq_max_k(lib):
     # the largest k the prefill path accepts (2^20): the staging offsets of the
     # last blocks and the past-the-end prefetch stay inside 32 bits

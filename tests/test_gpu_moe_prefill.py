@@ -37,7 +37,7 @@ def moe_config_banks():
     return synth.moe_banks(synth.MOE_DECODE, 64, 2048, 768)
 
 
-@pytest.mark.parametrize("m", [64, 200, 512])
+@pytest.mark.parametrize("m", [64, 200, 512, 2048])
 def test_moe_prefill_routed_config(lib, moe_config_banks, m):
     # the routed-MoE workload's experts and router (64 experts, top-8,
     # 2048/768) at prefill token counts
