@@ -72,6 +72,16 @@ def test_q8_gemv_many_workgroups(lib, m, n, k):
     check(lib, w, qs, d16, s, n, k)
 
 
+@pytest.mark.parametrize("m", [1, 4, 8])
+@pytest.mark.parametrize("n,k", [(4096, 4096), (11008, 4096), (4096, 11008)])
+def test_q8_gemv_sweep_full_size(lib, m, n, k):
+    # the three sweep matrices at the token counts bench.py times
+    say(f"q8 gemv sweep shape m={m} n={n} k={k}")
+    w = synth.random_q4k(synth.rng(95, 1, n + 7 * k), n, k)
+    qs, d16, s = quantised(m, k, 7 + m)
+    check(lib, w, qs, d16, s, n, k)
+
+
 @pytest.mark.parametrize("m,n,k", [(8, 11008, 4096), (4, 4096, 11008)])
 def test_q8_gemv_decode_shapes(lib, m, n, k):
     # the 7B-style decode projections, checked against the oracle and against
