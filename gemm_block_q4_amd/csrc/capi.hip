@@ -683,10 +683,13 @@ int ffn_common(const void* w_gate, const void* w_up, const void* w_down, int n_e
   const int cus = device_cus();
   const int rt = inter / 64, tt = (m + 127) / 128;
   const long long gu_tiles = static_cast<long long>(rt) * tt;
+  const int kb_all = hidden / Q4K_QK;
   int tail = 0, tsplit = 1;
   if (cus > 0 && gu_tiles > cus && gu_tiles % cus != 0) {
     tail = static_cast<int>((gu_tiles % cus + tt - 1) / tt);
-    tsplit = std::min({4, hidden / Q4K_QK, cus / (tail * tt), rt / (2 * tail)});
+    tsplit = std::min({4, kb_all, cus / (tail * tt), rt / (2 * tail)});
+    // every split owns at least one block (e.g. 5 blocks: 3 splits, not 4)
+    while (tsplit > 1 && (tsplit - 1) * ((kb_all + tsplit - 1) / tsplit) >= kb_all) --tsplit;
     if (tsplit < 2) tail = 0;
   }
   if (tail > 0) {
@@ -699,7 +702,7 @@ int ffn_common(const void* w_gate, const void* w_up, const void* w_down, int n_e
     tp.row_tile0 = rt - tail;
     tp.row_tiles = tail;
     tp.splits = tsplit;
-    tp.split_blocks = (hidden / Q4K_QK + tsplit - 1) / tsplit;
+    tp.split_blocks = (kb_all + tsplit - 1) / tsplit;
     if ((e = launch_mmq(tp, s)) != hipSuccess) return Q4K_ERR_LAUNCH;
     if ((e = launch_mmq_gu_finish(parts, tsplit, m, tail * 64, (rt - tail) * 64, inter, qh, dh, s)) !=
         hipSuccess)

@@ -188,11 +188,12 @@ def test_decode_q8_ffn_shapes(lib, m, hidden, inter, bf16):
     assert np.all(np.isfinite(y))
 
 
-@pytest.mark.parametrize("m,hidden", [(130, 512), (300, 1024)])
+@pytest.mark.parametrize("m,hidden", [(130, 512), (300, 1024), (130, 1280)])
 def test_prefill_ffn_gate_up_tail_split(lib, m, hidden):
     # 272 row tiles of the fused gate/up pass x 2 or 3 token tiles leave a
     # partial last round on 256 compute units: the last 16 row tiles run as a
-    # k-split pass (2 and 4 splits, the last token tile ragged) whose gate and
+    # k-split pass (2, 4 and 3 splits: 5 blocks of k cannot go into 4
+    # non-empty splits; the last token tile ragged) whose gate and
     # up sums are added by the finishing kernel; every fifth token (every
     # lane position of a token tile over the sample) and the last are compared
     inter = 17408
